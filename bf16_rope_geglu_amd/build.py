@@ -1,0 +1,45 @@
+"""Build lib/librgg.so: the HIP kernels and the C ABI, for gfx950 only.
+
+    python -m bf16_rope_geglu_amd.build
+
+Flags: -ffp-contract=off keeps every multiply and add a separate IEEE op
+(the bf16 rounding sits between them); packed-fp32 instructions are disabled;
+symbols other than the C ABI are hidden.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIBDIR = os.path.join(HERE, "lib")
+LIBRARY = os.path.join(LIBDIR, "librgg.so")
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "capi.cpp")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fvisibility=hidden",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def build(out=LIBRARY, extra=()):
+    """Compile the library to `out` (always recompiles); return its path."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + proc.stdout + proc.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,308 @@
+// C ABI of the fused RoPE / GEGLU path: argument checks, overlap analysis,
+// per-device set-up, and the kernel launches (declared in include/rgg.h).
+//
+// Every check runs on the host before anything is enqueued; a failing check
+// returns its status and touches no device state.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <mutex>
+
+#include <hip/hip_runtime_api.h>
+
+#include "launch.h"
+#include "layout.h"
+#include "rgg.h"
+
+namespace {
+
+using rgg::FastDiv;
+using rgg::make_fastdiv;
+using rgg::Layout;
+using rgg::make_layout;
+using rgg::may_overlap;
+using rgg::rows_disjoint;
+
+constexpr int64_t kMax32 = (int64_t)1 << 31;  // index math in the kernels is 32-bit
+
+bool aligned16(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// ---------------------------------------------------------------------------
+// per-device state: compute-unit count and the GELU table
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+    std::mutex lock;
+    std::atomic<int> table_ready{0};
+    std::atomic<int> cus{0};
+};
+
+DeviceState g_devices[kMaxDevices];
+
+int current_device(int &dev)
+{
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return RGG_ERR_HIP;
+    return RGG_OK;
+}
+
+int cu_count(int dev)
+{
+    int c = g_devices[dev].cus.load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            c = 256;
+        g_devices[dev].cus.store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
+// Builds the GELU table of the current device `dev` on `stream` and waits.
+int ensure_table(int dev, hipStream_t stream)
+{
+    DeviceState &d = g_devices[dev];
+    if (d.table_ready.load(std::memory_order_acquire))
+        return RGG_OK;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess)
+        return RGG_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone)
+        return RGG_ERR_CAPTURING;
+    std::lock_guard<std::mutex> g(d.lock);
+    if (d.table_ready.load(std::memory_order_acquire))
+        return RGG_OK;
+    if (rgg::launch_build_gelu_table(stream) != hipSuccess)
+        return RGG_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess)
+        return RGG_ERR_HIP;
+    d.table_ready.store(1, std::memory_order_release);
+    return RGG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rgg_status_string(int status)
+{
+    switch (status) {
+    case RGG_OK:
+        return "ok";
+    case RGG_ERR_NULL:
+        return "a required pointer is NULL";
+    case RGG_ERR_SHAPE:
+        return "invalid shape, stride or view count";
+    case RGG_ERR_UNSUPPORTED:
+        return "layout outside the 8-element vector contract";
+    case RGG_ERR_ALIGN:
+        return "pointer not 16-byte aligned or stride not a multiple of the vector";
+    case RGG_ERR_ALIAS:
+        return "an output overlaps an input or another output";
+    case RGG_ERR_HIP:
+        return "HIP runtime error";
+    case RGG_ERR_CAPTURING:
+        return "GELU table not built on this device and the stream is capturing; "
+               "call rgg_prepare_device first";
+    default:
+        return "unknown status";
+    }
+}
+
+int rope_cossin_precompute(const float *freqs, int64_t S, int64_t B, int64_t R,
+                           int64_t stride_s, int64_t stride_b, uint16_t *cos_out,
+                           uint16_t *sin_out, hipStream_t stream)
+{
+    if (S < 0 || B < 0 || R < 0 || stride_s < 0 || stride_b < 0)
+        return RGG_ERR_SHAPE;
+    if (R % 8 != 0)
+        return RGG_ERR_UNSUPPORTED;
+    if (S == 0 || B == 0 || R == 0)
+        return RGG_OK;
+    if (!freqs || !cos_out || !sin_out)
+        return RGG_ERR_NULL;
+    if (!aligned16(freqs) || !aligned16(cos_out) || !aligned16(sin_out) || stride_s % 4 != 0 ||
+        stride_b % 4 != 0)
+        return RGG_ERR_ALIGN;
+    if (S * B >= kMax32 || S * B * (R / 8) >= kMax32)
+        return RGG_ERR_UNSUPPORTED;
+
+    const int64_t fn[2] = {S, B}, fst[2] = {stride_s, stride_b};
+    const int64_t tn[1] = {B * S}, tst[1] = {R};
+    Layout lf = make_layout(freqs, 4, 2, fn, fst, R);
+    Layout lc = make_layout(cos_out, 2, 1, tn, tst, R);
+    Layout ls = make_layout(sin_out, 2, 1, tn, tst, R);
+    if (may_overlap(lc, ls) || may_overlap(lc, lf) || may_overlap(ls, lf))
+        return RGG_ERR_ALIAS;
+
+    rgg::CosSinParams p;
+    p.freqs = freqs;
+    p.cos = cos_out;
+    p.sin = sin_out;
+    p.stride_s = stride_s;
+    p.stride_b = stride_b;
+    p.vec_total = (uint32_t)(S * B * (R / 8));
+    p.R = (int32_t)R;
+    p.div_vecs = make_fastdiv((uint32_t)(R / 8));
+    p.div_s = make_fastdiv((uint32_t)S);
+    return rgg::launch_rope_cossin(p, stream) == hipSuccess ? RGG_OK : RGG_ERR_HIP;
+}
+
+int rope_rotate_half_bf16(const rgg_rope_view *views, int n_views, int64_t B, int64_t S,
+                          int64_t H, int64_t D, int64_t R, const uint16_t *cos,
+                          const uint16_t *sin, hipStream_t stream)
+{
+    if (n_views < 1 || n_views > rgg::kMaxViews || B < 0 || S < 0 || H < 0 || D <= 0 || R < 0 ||
+        R > D || R % 2 != 0)
+        return RGG_ERR_SHAPE;
+    if (!views)
+        return RGG_ERR_NULL;
+    for (int v = 0; v < n_views; ++v) {
+        const rgg_rope_view &V = views[v];
+        if (V.x_stride_b < 0 || V.x_stride_s < 0 || V.x_stride_h < 0 || V.out_stride_b < 0 ||
+            V.out_stride_s < 0 || V.out_stride_h < 0)
+            return RGG_ERR_SHAPE;
+    }
+    if (D % 8 != 0 || R % 16 != 0)
+        return RGG_ERR_UNSUPPORTED;
+    if (B == 0 || S == 0 || H == 0)
+        return RGG_OK;
+    if (B * S >= kMax32 || D > 8192 || H * D >= kMax32 / 64)
+        return RGG_ERR_UNSUPPORTED;
+    if (R > 0 && (!cos || !sin))
+        return RGG_ERR_NULL;
+    if (R > 0 && (!aligned16(cos) || !aligned16(sin)))
+        return RGG_ERR_ALIGN;
+
+    const int64_t n3[3] = {B, S, H};
+    Layout lx[rgg::kMaxViews], lo[rgg::kMaxViews];
+    bool in_place[rgg::kMaxViews];
+    for (int v = 0; v < n_views; ++v) {
+        const rgg_rope_view &V = views[v];
+        if (!V.x || !V.out)
+            return RGG_ERR_NULL;
+        if (!aligned16(V.x) || !aligned16(V.out) || V.x_stride_b % 8 || V.x_stride_s % 8 ||
+            V.x_stride_h % 8 || V.out_stride_b % 8 || V.out_stride_s % 8 || V.out_stride_h % 8)
+            return RGG_ERR_ALIGN;
+        const int64_t xs[3] = {V.x_stride_b, V.x_stride_s, V.x_stride_h};
+        const int64_t os[3] = {V.out_stride_b, V.out_stride_s, V.out_stride_h};
+        lx[v] = make_layout(V.x, 2, 3, n3, xs, D);
+        lo[v] = make_layout(V.out, 2, 3, n3, os, D);
+        if (!rows_disjoint(lo[v]))
+            return RGG_ERR_UNSUPPORTED;
+        in_place[v] = V.x == V.out && V.x_stride_b == V.out_stride_b &&
+                      V.x_stride_s == V.out_stride_s && V.x_stride_h == V.out_stride_h;
+    }
+    if (R > 0) {
+        const int64_t tn[1] = {B * S}, tst[1] = {R};
+        Layout lc = make_layout(cos, 2, 1, tn, tst, R);
+        Layout ls = make_layout(sin, 2, 1, tn, tst, R);
+        for (int v = 0; v < n_views; ++v)
+            if (may_overlap(lo[v], lc) || may_overlap(lo[v], ls))
+                return RGG_ERR_ALIAS;
+    }
+    for (int v = 0; v < n_views; ++v) {
+        for (int w = 0; w < n_views; ++w) {
+            if (w == v ? !in_place[v] && may_overlap(lo[v], lx[w]) : may_overlap(lo[v], lx[w]))
+                return RGG_ERR_ALIAS;
+            if (w > v && may_overlap(lo[v], lo[w]))
+                return RGG_ERR_ALIAS;
+        }
+    }
+
+    rgg::RopeParams p;
+    memset(&p, 0, sizeof p);
+    p.tail_mask = 0;
+    for (int v = 0; v < n_views; ++v) {
+        const rgg_rope_view &V = views[v];
+        p.v[v] = rgg::RopeView{V.x, V.out, V.x_stride_b, V.x_stride_s, V.x_stride_h,
+                               V.out_stride_b, V.out_stride_s, V.out_stride_h};
+        if (!in_place[v])
+            p.tail_mask |= 1 << v;
+    }
+    p.cos = cos;
+    p.sin = sin;
+    p.tokens = B * S;
+    p.n_views = n_views;
+    p.S = (int32_t)S;
+    p.H = (int32_t)H;
+    p.D = (int32_t)D;
+    p.R = (int32_t)R;
+    p.half = (int32_t)(R / 2);
+    p.tok_per_wg = rgg::rope_tokens_per_workgroup(n_views, (int)H, (int)D, (int)R);
+    p.div_s = make_fastdiv((uint32_t)S);
+    p.div_pairs = make_fastdiv(R >= 16 ? (uint32_t)(R / 16) : 1u);
+    p.div_heads = make_fastdiv((uint32_t)H);
+    p.div_tail = make_fastdiv(D > R ? (uint32_t)((D - R) / 8) : 1u);
+    if (R == 0 && p.tail_mask == 0)
+        return RGG_OK;
+    return rgg::launch_rope_rotate_half(p, stream) == hipSuccess ? RGG_OK : RGG_ERR_HIP;
+}
+
+int gelu_and_mul_bf16(const uint16_t *input, int64_t rows, int64_t hidden, int64_t in_row_stride,
+                      uint16_t *out, int64_t out_row_stride, hipStream_t stream)
+{
+    if (rows < 0 || hidden < 0 || in_row_stride < 0 || out_row_stride < 0)
+        return RGG_ERR_SHAPE;
+    if (hidden % 8 != 0)
+        return RGG_ERR_UNSUPPORTED;
+    if (rows > 1 && out_row_stride < hidden)
+        return RGG_ERR_UNSUPPORTED;
+    if (rows == 0 || hidden == 0)
+        return RGG_OK;
+    if (!input || !out)
+        return RGG_ERR_NULL;
+    if (!aligned16(input) || !aligned16(out) || in_row_stride % 8 || out_row_stride % 8)
+        return RGG_ERR_ALIGN;
+    if (rows * (hidden / 8) >= kMax32)
+        return RGG_ERR_UNSUPPORTED;
+
+    const int64_t rn[1] = {rows};
+    const int64_t is[1] = {in_row_stride}, os[1] = {out_row_stride};
+    Layout li = make_layout(input, 2, 1, rn, is, 2 * hidden);
+    Layout lo = make_layout(out, 2, 1, rn, os, hidden);
+    bool in_place = out == input && out_row_stride == in_row_stride;
+    if (!in_place && may_overlap(lo, li))
+        return RGG_ERR_ALIAS;
+
+    int dev;
+    if (current_device(dev) != RGG_OK)
+        return RGG_ERR_HIP;
+    int st = ensure_table(dev, stream);
+    if (st != RGG_OK)
+        return st;
+
+    rgg::GegluParams p;
+    p.in = input;
+    p.out = out;
+    p.in_stride = in_row_stride;
+    p.out_stride = out_row_stride;
+    p.vec_total = (uint32_t)(rows * (hidden / 8));
+    p.hidden = (int32_t)hidden;
+    p.div_vecs = make_fastdiv((uint32_t)(hidden / 8));
+    int grid = rgg::geglu_grid(p.vec_total, cu_count(dev));
+    return rgg::launch_gelu_and_mul(p, grid, stream) == hipSuccess ? RGG_OK : RGG_ERR_HIP;
+}
+
+int rgg_prepare_device(int device)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return RGG_ERR_SHAPE;
+    int prev;
+    if (hipGetDevice(&prev) != hipSuccess)
+        return RGG_ERR_HIP;
+    if (hipSetDevice(device) != hipSuccess)
+        return RGG_ERR_HIP;
+    int st = ensure_table(device, nullptr);
+    if (hipSetDevice(prev) != hipSuccess && st == RGG_OK)
+        st = RGG_ERR_HIP;
+    return st;
+}
+
+}  // extern "C"

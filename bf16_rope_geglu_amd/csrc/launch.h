@@ -1,0 +1,85 @@
+// Internal interface between the C ABI layer (capi.cpp) and the HIP kernels
+// (kernels.hip).  Parameter blocks are passed to the kernels by value.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace rgg {
+
+// Unsigned division of n < 2^31 by a fixed d >= 1 with one multiply-high,
+// shift and add: Granlund & Montgomery, "Division by Invariant Integers using
+// Multiplication" (PLDI 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((1ull << l) < d)
+        ++l;
+    uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)m, l};
+}
+
+constexpr int kMaxViews = 4;
+constexpr int kThreads = 256;  // one workgroup = four wave64s
+
+struct RopeView {
+    const uint16_t *x;
+    uint16_t *out;
+    int64_t xs_b, xs_s, xs_h;
+    int64_t os_b, os_s, os_h;
+};
+
+struct RopeParams {
+    RopeView v[kMaxViews];
+    const uint16_t *cos;
+    const uint16_t *sin;
+    int64_t tokens;        // B * S
+    int32_t n_views;
+    int32_t S;             // only used through div_s
+    int32_t H, D, R;
+    int32_t half;          // R / 2
+    int32_t tok_per_wg;    // tokens handled by one workgroup
+    int32_t tail_mask;     // bit v set: copy the tail of view v
+    FastDiv div_s;         // token -> (b, s)
+    FastDiv div_pairs;     // rotation item -> (token-local, head, pair); divisor R/16
+    FastDiv div_heads;     // divisor H
+    FastDiv div_tail;      // divisor (D - R) / 8
+};
+
+struct CosSinParams {
+    const float *freqs;
+    uint16_t *cos;
+    uint16_t *sin;
+    int64_t stride_s, stride_b;
+    uint32_t vec_total;    // B * S * R / 8
+    int32_t R;
+    FastDiv div_vecs;      // divisor R / 8: vector -> (row, column group)
+    FastDiv div_s;         // row -> (b, s)
+};
+
+struct GegluParams {
+    const uint16_t *in;
+    uint16_t *out;
+    int64_t in_stride, out_stride;
+    uint32_t vec_total;    // rows * hidden / 8
+    int32_t hidden;
+    FastDiv div_vecs;      // divisor hidden / 8: vector -> (row, column group)
+};
+
+// Launchers: enqueue on `stream`, return the hipError_t of the launch.
+hipError_t launch_rope_cossin(const CosSinParams &p, hipStream_t stream);
+hipError_t launch_rope_rotate_half(const RopeParams &p, hipStream_t stream);
+hipError_t launch_gelu_and_mul(const GegluParams &p, int grid, hipStream_t stream);
+hipError_t launch_build_gelu_table(hipStream_t stream);
+
+// Tunables chosen by the host layer.
+int rope_tokens_per_workgroup(int n_views, int H, int D, int R);
+int geglu_grid(uint32_t vec_total, int cu_count);
+
+}  // namespace rgg

@@ -1,0 +1,161 @@
+/*
+ * rgg.h -- C ABI of bf16_rope_geglu_amd: the fused elementwise path of an
+ * ERNIE-Image style diffusion transformer, for AMD Instinct MI355X (gfx950).
+ *
+ * The method comes from the page "[sglang] ERNIE-Image의 RoPE와 GELU-mul 융합
+ * 및 RoPE cos/sin 호이스팅을 통한 성능 최적화" (blog.secrett2633.cloud, an
+ * analysis of sglang PR 34306), cited below as [ERNIE-fuse] with its section:
+ *   §1 hoist the rotary cos/sin tables once per forward,
+ *   §2 fuse the rotate-half RoPE chain, bit-exact with eager bf16 rounding,
+ *   §3 fuse GEGLU (up * gelu(gate)) keeping eager's bf16 activation rounding.
+ *
+ * Conventions shared by every entry point
+ *   - bf16 data is passed as uint16_t bit patterns (the upper half of an IEEE
+ *     binary32); fp32 data as float.
+ *   - Every tensor pointer is device memory owned by the caller.  No call
+ *     allocates memory.  The one piece of library state is a constant
+ *     7 KiB GELU table per device, built on the first GEGLU call on that
+ *     device (or by rgg_prepare_device) and kept until the process ends.
+ *   - Sizes and strides count elements, not bytes.  Strides must be >= 0.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream) of the
+ *     current HIP device.  Arguments are checked synchronously first; on any
+ *     error nothing is enqueued and a nonzero rgg_status is returned.  No C++
+ *     exception crosses this interface.
+ *   - Vector access: bf16 base pointers must be 16-byte aligned and bf16
+ *     strides multiples of 8 elements (RGG_ERR_ALIGN otherwise); the fp32
+ *     angle tensor needs 16-byte alignment and strides that are multiples of
+ *     4.  There is no slower fallback for other layouts.
+ *   - A size of zero in any batch-like dimension is a valid no-op.
+ */
+#ifndef RGG_H
+#define RGG_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RGG_API __attribute__((visibility("default")))
+
+typedef enum rgg_status {
+    RGG_OK = 0,
+    RGG_ERR_NULL = 1,        /* a pointer needed for a non-empty call is NULL */
+    RGG_ERR_SHAPE = 2,       /* negative size/stride, odd R, R > D, n_views out of 1..4 */
+    RGG_ERR_UNSUPPORTED = 3, /* width not a multiple of the 8-element vector, or an output
+                                view whose rows overlap themselves */
+    RGG_ERR_ALIGN = 4,       /* base pointer or stride breaks the 16-byte vector rule */
+    RGG_ERR_ALIAS = 5,       /* an output overlaps an input or another output (other than
+                                the exact in-place forms each call allows) */
+    RGG_ERR_HIP = 6,         /* the HIP runtime reported an error */
+    RGG_ERR_CAPTURING = 7    /* first GEGLU call on a device made while `stream` is being
+                                captured: call rgg_prepare_device() before capturing */
+} rgg_status;
+
+/*
+ * (a1) Hoisted rotary tables.        [ERNIE-fuse §1, _precompute_rope_cos_sin]
+ *
+ * The rotary angles `freqs` have the page's shape (S, B, 1, R) in fp32: the
+ * angle of sequence position s, batch row b, rotary column j is
+ *     freqs[s * stride_s + b * stride_b + j]      (unit stride along j).
+ * Writes two contiguous bf16 tables of shape (B*S, R), row b*S + s (the
+ * page's permute to (B, S, 1, R) followed by a flatten):
+ *     cos_out[(b*S + s)*R + j] = rne_bf16(cos(angle)),
+ *     sin_out[(b*S + s)*R + j] = rne_bf16(sin(angle)).
+ * Each entry is the exact cosine/sine of the fp32 angle rounded once to the
+ * nearest bf16 (ties to even).  The tables depend only on the angles, so one
+ * call per forward serves every layer and projection.
+ *
+ * Requirements: S, B >= 0; R >= 0 and a multiple of 8; freqs 16-byte aligned
+ * with stride_s, stride_b multiples of 4; cos_out, sin_out 16-byte aligned;
+ * the two tables may not overlap each other or freqs.
+ */
+RGG_API int rope_cossin_precompute(const float *freqs, int64_t S, int64_t B, int64_t R,
+                           int64_t stride_s, int64_t stride_b,
+                           uint16_t *cos_out, uint16_t *sin_out, hipStream_t stream);
+
+/*
+ * One strided (B, S, H, D) bf16 tensor to rotate and where to put the result.
+ * Element (b, s, h, d) of the input is x[b*x_stride_b + s*x_stride_s +
+ * h*x_stride_h + d]; the output uses the out_* strides the same way.  A view
+ * may be a slice of a larger buffer, e.g. the q or k part of a fused QKV
+ * projection output, read in place without a copy.
+ */
+typedef struct rgg_rope_view {
+    const uint16_t *x;
+    uint16_t *out;
+    int64_t x_stride_b, x_stride_s, x_stride_h;
+    int64_t out_stride_b, out_stride_s, out_stride_h;
+} rgg_rope_view;
+
+/*
+ * (a2, a3) Rotate-half RoPE with tail passthrough.          [ERNIE-fuse §2]
+ *
+ * For every view v, token (b, s), head h, with c and s the bf16 rows b*S + s
+ * of `cos` and `sin` (contiguous (B*S, R)) and h2 = R/2:
+ *   j <  h2:      out[j] = rne(rne(x[j]*c[j]) + rne(-x[j+h2]*s[j]))
+ *   h2 <= j < R:  out[j] = rne(rne(x[j]*c[j]) + rne( x[j-h2]*s[j]))
+ *   R <= j < D:   out[j] = x[j]                       (bits copied)
+ * i.e. exactly the eager bf16 chunk / neg / cat / mul / mul / add chain
+ * followed by the tail concatenation, every op rounded to nearest-even bf16.
+ * c[j] and c[j + h2] are used as given (they need not be equal).
+ *
+ * `views` is a host array of n_views (1..4) entries, read during the call;
+ * all views share B, S, H, D, R and the cos/sin tables (q and k of a layer
+ * in one launch).  Out of place, or in place when out == x with identical
+ * strides (the tail is then left untouched).  No output may overlap any
+ * input or another output otherwise; the check is exact for views with equal
+ * strides (e.g. q/k/v slices of one fused buffer) and by address range for
+ * views with different strides.
+ *
+ * Requirements: B, S, H >= 0; D > 0 and a multiple of 8; R even with
+ * 0 <= R <= D and R a multiple of 16 (each half a whole number of 8-element
+ * vectors); R = 0 copies x.  Output rows must not overlap each other.
+ */
+RGG_API int rope_rotate_half_bf16(const rgg_rope_view *views, int n_views, int64_t B, int64_t S,
+                          int64_t H, int64_t D, int64_t R, const uint16_t *cos,
+                          const uint16_t *sin, hipStream_t stream);
+
+/*
+ * (a4, a5) GEGLU with activation rounding.                  [ERNIE-fuse §3]
+ *
+ * `input` is (rows, 2*hidden) bf16 with row stride in_row_stride: the first
+ * `hidden` columns are the gate, the next `hidden` the up projection.  Writes
+ * (rows, hidden) bf16 to `out` with row stride out_row_stride:
+ *   out[r][j] = rne_bf16( up[r][j] * G(gate[r][j]) ),
+ *   G(x)      = rne_bf16( x * Phi(x) ),  Phi the standard normal CDF
+ * (the exact-erf GELU rounded to bf16 before the multiply, as the eager
+ * up * F.gelu(gate) chain rounds it).  G is correctly rounded for every one
+ * of the 65536 bf16 inputs: G(+-0) = +-0, G(+inf) = +inf, G(-inf) = NaN,
+ * G(NaN) = NaN.
+ *
+ * In place is allowed in one form: out == input with out_row_stride ==
+ * in_row_stride (the result overwrites the gate half).  Otherwise out may not
+ * overlap input.
+ *
+ * Requirements: rows, hidden >= 0; hidden a multiple of 8; strides multiples
+ * of 8 with out_row_stride >= hidden when rows > 1; 16-byte aligned bases.
+ */
+RGG_API int gelu_and_mul_bf16(const uint16_t *input, int64_t rows, int64_t hidden,
+                      int64_t in_row_stride, uint16_t *out, int64_t out_row_stride,
+                      hipStream_t stream);
+
+/*
+ * Builds the constant GELU table on HIP device `device` now (synchronously)
+ * if it is not built yet.  Needed only before capturing a GEGLU call into a
+ * HIP graph on a device that has not run one; otherwise the first
+ * gelu_and_mul_bf16 call on the device does it.  Leaves the current device
+ * unchanged.
+ */
+RGG_API int rgg_prepare_device(int device);
+
+/* Static, human-readable text for a status code (never NULL). */
+RGG_API const char *rgg_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RGG_H */

@@ -1,0 +1,178 @@
+"""The C ABI on the host, without a GPU.
+
+Covers: the library loads and exports every function include/rgg.h declares,
+status strings, every argument check that returns before anything is
+enqueued (made with fake device addresses, which are never dereferenced),
+the overlap analysis against brute force (host-only C++ under ASan/UBSan),
+and the Python binding's own argument checks.  No call here reaches a launch.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import bf16_rope_geglu_amd as rgg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rgg.h")
+
+OK, NULL, SHAPE, UNSUPPORTED, ALIGN, ALIAS, HIP, CAPTURING = range(8)
+A = 0x7F0000000000  # a 16-byte aligned fake device address
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    return re.findall(r"RGG_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rgg.LIBRARY):
+        import bf16_rope_geglu_amd.build as b
+        b.build()
+    return rgg.library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == {"rope_cossin_precompute", "rope_rotate_half_bf16", "gelu_and_mul_bf16",
+                          "rgg_prepare_device", "rgg_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", rgg.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.rgg_status_string(code)
+        assert s and s.decode() != "unknown status"
+    assert lib.rgg_status_string(99).decode() == "unknown status"
+
+
+def cossin(lib, freqs=A, S=4, B=2, R=8, ss=16, sb=8, cos=A + 4096, sin=A + 8192):
+    return lib.rope_cossin_precompute(freqs, S, B, R, ss, sb, cos, sin, None)
+
+
+def test_cossin_checks(lib):
+    assert cossin(lib, freqs=None) == NULL
+    assert cossin(lib, cos=None) == NULL
+    assert cossin(lib, S=-1) == SHAPE
+    assert cossin(lib, ss=-4) == SHAPE
+    assert cossin(lib, R=12) == UNSUPPORTED
+    assert cossin(lib, freqs=A + 4) == ALIGN
+    assert cossin(lib, cos=A + 4096 + 2) == ALIGN
+    assert cossin(lib, ss=18) == ALIGN
+    assert cossin(lib, sin=A + 4096 + 16) == ALIAS   # tables overlap
+    assert cossin(lib, cos=A + 16) == ALIAS          # table over the angles
+    assert cossin(lib, S=0) == OK
+    assert cossin(lib, B=0, freqs=None) == OK
+    assert cossin(lib, R=0) == OK
+
+
+def view(x=A, out=A + (1 << 24), xs=(8192, 1024, 128), os_=(8192, 1024, 128)):
+    return rgg.RopeView(x, out, *xs, *os_)
+
+
+def rope(lib, views, n=None, B=2, S=8, H=8, D=128, R=128, cos=A + (1 << 26),
+         sin=A + (1 << 26) + (1 << 20)):
+    arr = (rgg.RopeView * max(1, len(views)))(*views)
+    n = len(views) if n is None else n
+    return lib.rope_rotate_half_bf16(arr if views else None, n, B, S, H, D, R, cos, sin, None)
+
+
+def test_rope_checks(lib):
+    v = view()
+    assert rope(lib, [v], n=0) == SHAPE
+    assert rope(lib, [v], n=5) == SHAPE
+    assert rope(lib, [v], R=3) == SHAPE
+    assert rope(lib, [v], R=144) == SHAPE             # R > D
+    assert rope(lib, [v], B=-1) == SHAPE
+    assert rope(lib, [view(xs=(8192, -1024, 128))]) == SHAPE
+    assert rope(lib, [v], D=12, R=0) == UNSUPPORTED
+    assert rope(lib, [v], R=24, D=32) == UNSUPPORTED  # half not a whole vector
+    assert rope(lib, [], n=1) == NULL
+    assert rope(lib, [view(x=None)]) == NULL
+    assert rope(lib, [v], cos=None) == NULL
+    assert rope(lib, [view(x=A + 8)]) == ALIGN
+    assert rope(lib, [view(xs=(8192, 1024, 132))]) == ALIGN
+    assert rope(lib, [v], sin=A + (1 << 26) + 2) == ALIGN
+    # output rows overlapping each other
+    assert rope(lib, [view(os_=(8192, 1024, 64))]) == UNSUPPORTED
+    # partial overlap of out and x, and of out and the tables
+    assert rope(lib, [view(out=A + 256)]) == ALIAS
+    assert rope(lib, [view(out=A + (1 << 26))]) == ALIAS
+    # two views writing the same place; one view's out over another's x
+    assert rope(lib, [view(), view(x=A + (1 << 22))]) == ALIAS
+    assert rope(lib, [view(), view(x=A + (1 << 22), out=A)]) == ALIAS
+    # empty is a no-op
+    assert rope(lib, [v], B=0) == OK
+    assert rope(lib, [v], S=0, cos=None, sin=None) == OK
+
+
+def gelu(lib, inp=A, rows=16, hidden=64, is_=128, out=A + (1 << 20), os_=64):
+    return lib.gelu_and_mul_bf16(inp, rows, hidden, is_, out, os_, None)
+
+
+def test_gelu_checks(lib):
+    assert gelu(lib, rows=-1) == SHAPE
+    assert gelu(lib, is_=-8) == SHAPE
+    assert gelu(lib, hidden=12) == UNSUPPORTED
+    assert gelu(lib, os_=56) == UNSUPPORTED
+    assert gelu(lib, inp=None) == NULL
+    assert gelu(lib, out=None) == NULL
+    assert gelu(lib, inp=A + 2) == ALIGN
+    assert gelu(lib, is_=132) == ALIGN
+    assert gelu(lib, out=A + 64) == ALIAS             # inside the input, not the in-place form
+    assert gelu(lib, out=A, os_=64) == ALIAS          # in place needs the input's row stride
+    assert gelu(lib, rows=0) == OK
+    assert gelu(lib, hidden=0, inp=None) == OK
+
+
+def test_prepare_device_bad_index(lib):
+    assert lib.rgg_prepare_device(-1) == SHAPE
+
+
+def test_overlap_analysis_bruteforce(tmp_path):
+    exe = os.path.join(tmp_path, "layout_check")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all",
+                    "-I", os.path.join(ROOT, "bf16_rope_geglu_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "host", "layout_check.cpp"), "-o", exe],
+                   check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.startswith("ok")
+
+
+def test_fastdiv_matches_division(tmp_path):
+    exe = os.path.join(tmp_path, "fastdiv_check")
+    subprocess.run(["g++", "-std=c++17", "-O2", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "bf16_rope_geglu_amd", "csrc"),
+                    "-I", "/opt/rocm/include",
+                    os.path.join(ROOT, "tests", "host", "fastdiv_check.cpp"), "-o", exe],
+                   check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
+
+
+def test_binding_rejects_host_tensors():
+    x = torch.zeros(1, 4, 2, 16, dtype=torch.bfloat16)
+    cs = torch.zeros(4, 16, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        rgg.rope_rotate_half_bf16(x, cs, cs)
+    with pytest.raises(TypeError):
+        rgg.gelu_and_mul_bf16(torch.zeros(4, 16, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        rgg.rope_cossin_precompute(torch.zeros(4, 1, 1, 16))
+
+
+def test_binding_error_carries_status(lib):
+    err = rgg.RggError("f", ALIAS, lib.rgg_status_string(ALIAS).decode())
+    assert err.status == ALIAS and "overlaps" in str(err)

@@ -1,0 +1,455 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI (needs a GPU).
+
+Bars, per step of the path:
+  rotate-half RoPE and the tail passthrough: bit-exact, every element;
+  cos/sin tables and GELU (transcendental stages): at most 1 bf16 ulp from
+  the oracle with at least 99.99% of elements bit-identical (mismatch counts
+  are printed; the kernels are designed to be correctly rounded, so the
+  expected count is 0);
+  GEGLU output: the oracle's bf16 product of up and the GPU's own GELU value
+  must match bit for bit, and the end-to-end output meets the 1-ulp bar.
+
+Inputs are the seeded workloads of workloads.py: the tiny workload whole, the
+two mid-size RoPE workloads whole, the full-size GEGLU and fused-QKV
+workloads on sampled rows (plus whole-tensor properties), and small
+adversarial shapes spanning several workgroups with ragged ends.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import bf16_rope_geglu_amd as rgg
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a HIP device")
+    assert os.path.exists(rgg.LIBRARY), "librgg.so is not built"
+    rgg.library()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a):
+    a = np.ascontiguousarray(a, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def ordered(bits):
+    b = np.asarray(bits, np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def assert_bitexact(got, want, what):
+    got, want = np.asarray(got), np.asarray(want)
+    bad = np.count_nonzero(got != want)
+    say(f"{what}: {got.size} elements, {bad} not bit-identical")
+    if bad:
+        idx = np.argwhere(got != want)[:5]
+        raise AssertionError(f"{what}: {bad} mismatches, first at {idx.tolist()}: "
+                             f"{[hex(int(got[tuple(i)])) for i in idx]} vs "
+                             f"{[hex(int(want[tuple(i)])) for i in idx]}")
+
+
+def assert_ulp_bar(got, want, what):
+    d = np.abs(ordered(got) - ordered(want))
+    bad = np.count_nonzero(got != want)
+    say(f"{what}: {got.size} elements, {bad} not bit-identical, max {int(d.max(initial=0))} ulp")
+    assert d.max(initial=0) <= 1, f"{what}: max ulp {d.max()}"
+    assert bad <= 1e-4 * got.size, f"{what}: {bad} of {got.size} not bit-identical"
+
+
+def with_guards(shape, fill=0x7FC1):
+    """A bf16 tensor of `shape` inside a buffer whose 4 KiB guard bands hold
+    a NaN pattern; returns (tensor, check) where check() verifies the bands."""
+    n = int(np.prod(shape))
+    g = 2048
+    buf = torch.full((n + 2 * g,), fill, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    t = buf[g:g + n].view(shape)
+
+    def check():
+        b = host(buf)
+        assert (b[:g] == fill).all() and (b[g + n:] == fill).all(), "write outside the output"
+    return t, check
+
+
+# ---------------------------------------------------------------------------
+# (a1) cos/sin tables
+# ---------------------------------------------------------------------------
+
+def gpu_cossin(freqs_np):
+    f = torch.from_numpy(np.ascontiguousarray(freqs_np)).cuda()
+    c, s = rgg.rope_cossin_precompute(f)
+    return host(c), host(s)
+
+
+@pytest.mark.parametrize("wid", [0, 1, 2, 4])
+def test_cossin_workload_tables(orc, wid):
+    say(f"cos/sin table, workload {wid}")
+    fr = W.workload_freqs(wid)
+    gc, gs = gpu_cossin(fr)
+    oc, os_ = orc.rope_cossin(fr)
+    assert_ulp_bar(gc, oc, f"cos w{wid}")
+    assert_ulp_bar(gs, os_, f"sin w{wid}")
+
+
+def test_cossin_adversarial(orc):
+    say("cos/sin adversarial angles, strided angles, per-batch angles")
+    rng = np.random.Generator(np.random.PCG64(9))
+    S, B, R = 37, 3, 24
+    fr = np.empty((S, B, 1, R), np.float32)
+    fr[:] = rng.uniform(-2e3, 2e3, fr.shape)
+    fr.reshape(-1)[:40] = [0.0, -0.0, 1e-30, -1e-30, 1e-7, np.pi, -np.pi, np.pi / 2, 1e4, -1e4,
+                           6e5, -6e5, 3e7, 1e-38, 2.0, 0.5, 100.0, 255.0, 63.0, 1.5707964,
+                           3.1415927, 4.712389, 6.2831855, 0.7853982, 1e5, 123456.0, 7.0, 11.0,
+                           0.1, 0.2, 0.3, 1.0, 2.5, 5.0, 10.0, 20.0, 50.0, 64.0, 128.0, 1000.0]
+    gc, gs = gpu_cossin(fr)
+    oc, os_ = orc.rope_cossin(fr)
+    assert_ulp_bar(gc, oc, "cos adversarial")
+    assert_ulp_bar(gs, os_, "sin adversarial")
+    # strided (non-contiguous) angle view and distinct angles per batch row
+    fr3 = W.freqs_3axis((2, 5, 7), (8, 12, 12), 3, batch_offsets=[0, 3, 9])
+    wide = np.zeros(fr3.shape[:3] + (fr3.shape[3] + 8,), np.float32)
+    wide[..., :fr3.shape[3]] = fr3
+    wt = torch.from_numpy(wide).cuda()[..., :fr3.shape[3]]
+    c, s = rgg.rope_cossin_precompute(wt)
+    oc, os_ = orc.rope_cossin(fr3)
+    assert_ulp_bar(host(c), oc, "cos strided")
+    assert_ulp_bar(host(s), os_, "sin strided")
+
+
+def test_cossin_empty_and_guards(orc):
+    say("cos/sin empty shapes and guard bands")
+    f = torch.zeros((0, 2, 1, 16), device="cuda")
+    c, s = rgg.rope_cossin_precompute(f)
+    assert c.shape == (0, 16)
+    fr = W.freqs_1d(33, 2, 16)
+    cg, ccheck = with_guards((66, 16))
+    sg, scheck = with_guards((66, 16))
+    rgg.rope_cossin_precompute(torch.from_numpy(fr).cuda(), cg, sg)
+    ccheck()
+    scheck()
+    oc, os_ = orc.rope_cossin(fr)
+    assert_ulp_bar(host(cg), oc, "cos guarded")
+    assert_ulp_bar(host(sg), os_, "sin guarded")
+
+
+# ---------------------------------------------------------------------------
+# (a2, a3) rotate-half RoPE
+# ---------------------------------------------------------------------------
+
+def oracle_rope(orc, x, cos, sin):
+    return orc.rope_rotate_half(x, cos, sin)
+
+
+def test_rope_tiny_workload(orc):
+    say("rope tiny workload")
+    r = W.WORKLOADS[0]["rope"]
+    fr = W.workload_freqs(0)
+    cos_d, sin_d = rgg.rope_cossin_precompute(torch.from_numpy(fr).cuda())
+    cos, sin = host(cos_d), host(sin_d)
+    x = W.normal_bf16((r["B"], r["S"], r["H"], r["D"]), W.seed_for(0, "x"))
+    out = rgg.rope_rotate_half_bf16(dev(x), cos_d, sin_d)
+    assert_bitexact(host(out), oracle_rope(orc, x, cos, sin), "rope tiny")
+    # end to end against the oracle's own tables
+    oc, os_ = orc.rope_cossin(fr)
+    assert_ulp_bar(host(out), oracle_rope(orc, x, oc, os_), "rope tiny end-to-end")
+
+
+@pytest.mark.parametrize("wid", [1, 2])
+def test_rope_workload_whole(orc, wid):
+    r = W.WORKLOADS[wid]["rope"]
+    B, S, H, D, R = r["B"], r["S"], r["H"], r["D"], r["R"]
+    say(f"rope workload {wid}: ({B},{S},{H},{D}) R={R} views={r['views']}")
+    fr = W.workload_freqs(wid)
+    cos_d, sin_d = rgg.rope_cossin_precompute(torch.from_numpy(fr).cuda())
+    cos, sin = host(cos_d), host(sin_d)
+    names = ["q", "k"][:r["views"]]
+    xs = [W.normal_bf16((B, S, H, D), W.seed_for(wid, n)) for n in names]
+    outs = rgg.rope_rotate_half_bf16([dev(x) for x in xs], cos_d, sin_d)
+    for n, x, o in zip(names, xs, outs):
+        got = host(o)
+        assert_bitexact(got, oracle_rope(orc, x, cos, sin), f"rope w{wid} {n}")
+        if R < D:
+            assert np.array_equal(got[..., R:], x[..., R:]), "tail must pass through"
+
+
+ADVERSARIAL = [  # B, S, H, D, R, views, data, tables
+    (3, 37, 5, 48, 32, 1, "special", "unpaired"),
+    (2, 129, 3, 64, 64, 2, "normal", "unpaired"),
+    (1, 300, 2, 32, 16, 3, "special", "special"),
+    (2, 17, 7, 128, 96, 4, "special", "unpaired"),
+    (1, 5, 1, 16, 0, 1, "normal", "none"),
+    (1, 1, 1, 16, 16, 1, "special", "special"),
+    (5, 3, 33, 24, 16, 2, "normal", "unpaired"),
+]
+
+
+@pytest.mark.parametrize("case", ADVERSARIAL, ids=lambda c: "B{}S{}H{}D{}R{}v{}".format(*c[:6]))
+def test_rope_adversarial(orc, case):
+    B, S, H, D, R, nv, kind, tkind = case
+    say(f"rope adversarial {case}")
+    seed = 7000 + B * 100 + S + H + D + R + nv
+    if tkind == "unpaired":
+        cos, sin = orc.rope_cossin(W.freqs_unpaired(S, B, R, seed))
+    elif tkind == "special":
+        cos = W.special_bf16((B * S, R), seed + 1)
+        sin = W.special_bf16((B * S, R), seed + 2)
+    else:
+        cos = np.zeros((B * S, 0), np.uint16)
+        sin = np.zeros((B * S, 0), np.uint16)
+    gen = W.special_bf16 if kind == "special" else W.normal_bf16
+    xs = [gen((B, S, H, D), seed + 10 + v) for v in range(nv)]
+    guarded = [with_guards((B, S, H, D)) for _ in range(nv)]
+    xd = [dev(x) for x in xs]
+    rgg.rope_rotate_half_bf16(xd, dev(cos) if R else torch.empty((B * S, 0), dtype=torch.bfloat16,
+                                                                  device="cuda"),
+                              dev(sin) if R else torch.empty((B * S, 0), dtype=torch.bfloat16,
+                                                             device="cuda"),
+                              out=[g[0] for g in guarded])
+    for v in range(nv):
+        guarded[v][1]()
+        assert np.array_equal(host(xd[v]), xs[v]), "input modified"
+        assert_bitexact(host(guarded[v][0]), oracle_rope(orc, xs[v], cos, sin), f"view {v}")
+
+
+def make_qkv(B, S, H, D, seed):
+    qkv = W.normal_bf16((B, S, 3 * H * D), seed)
+    return qkv
+
+
+def qkv_views(t, H, D):
+    B, S, _ = t.shape
+    q = t[..., :H * D].view(B, S, H, D)
+    k = t[..., H * D:2 * H * D].view(B, S, H, D)
+    return q, k
+
+
+def test_rope_fused_qkv_views_small(orc):
+    """q/k as strided views of a fused QKV buffer, out of place and in place."""
+    B, S, H, D, R = 2, 45, 4, 64, 64
+    say(f"rope fused qkv small ({B},{S},{H},{D})")
+    qkv = make_qkv(B, S, H, D, 8101)
+    cos, sin = orc.rope_cossin(W.freqs_unpaired(S, B, R, 8102))
+    t = dev(qkv)
+    q, k = qkv_views(t, H, D)
+    assert q.stride() == (S * 3 * H * D, 3 * H * D, D, 1)
+    oq, ok = rgg.rope_rotate_half_bf16([q, k], dev(cos), dev(sin))
+    hq = qkv[..., :H * D].reshape(B, S, H, D)
+    hk = qkv[..., H * D:2 * H * D].reshape(B, S, H, D)
+    assert_bitexact(host(oq), oracle_rope(orc, hq, cos, sin), "q from qkv")
+    assert_bitexact(host(ok), oracle_rope(orc, hk, cos, sin), "k from qkv")
+    # in place inside the fused buffer; v must be untouched
+    rgg.rope_rotate_half_bf16([q, k], dev(cos), dev(sin), out=[q, k])
+    after = host(t)
+    assert np.array_equal(after[..., :H * D].reshape(B, S, H, D), host(oq))
+    assert np.array_equal(after[..., H * D:2 * H * D].reshape(B, S, H, D), host(ok))
+    assert np.array_equal(after[..., 2 * H * D:], qkv[..., 2 * H * D:]), "v modified"
+
+
+def test_rope_partial_in_place_keeps_tail(orc):
+    B, S, H, D, R = 2, 19, 3, 128, 96
+    say("rope partial in place")
+    x = W.special_bf16((B, S, H, D), 8201)
+    cos, sin = orc.rope_cossin(W.freqs_unpaired(S, B, R, 8202))
+    t = dev(x)
+    rgg.rope_rotate_half_bf16(t, dev(cos), dev(sin), out=t)
+    assert_bitexact(host(t), oracle_rope(orc, x, cos, sin), "in place with tail")
+
+
+def test_rope_empty_shapes():
+    say("rope empty shapes")
+    c = torch.zeros((0, 16), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((0, 4, 2, 16), dtype=torch.bfloat16, device="cuda")
+    assert rgg.rope_rotate_half_bf16(x, c, c).shape == x.shape
+    x = torch.zeros((2, 0, 2, 16), dtype=torch.bfloat16, device="cuda")
+    assert rgg.rope_rotate_half_bf16(x, c, c).shape == x.shape
+    x = torch.zeros((1, 3, 0, 16), dtype=torch.bfloat16, device="cuda")
+    c3 = torch.zeros((3, 16), dtype=torch.bfloat16, device="cuda")
+    assert rgg.rope_rotate_half_bf16(x, c3, c3).shape == x.shape
+
+
+def test_rope_on_side_stream(orc):
+    say("rope on a non-default stream")
+    B, S, H, D, R = 1, 64, 4, 32, 32
+    x = W.normal_bf16((B, S, H, D), 8301)
+    cos, sin = orc.rope_cossin(W.freqs_unpaired(S, B, R, 8302))
+    xd, cd, sd = dev(x), dev(cos), dev(sin)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        out = rgg.rope_rotate_half_bf16(xd, cd, sd)
+    st.synchronize()
+    assert_bitexact(host(out), oracle_rope(orc, x, cos, sin), "side stream")
+
+
+def test_rope_dit_layer_full_size(orc):
+    """Full-size fused-QKV workload in the launch configuration the benchmark
+    times: q and k strided views of (4, 8192, 3*32*128), contiguous outputs,
+    one launch.  The whole cos/sin table is compared; RoPE on sampled tokens
+    (all heads of each) against the oracle's rows form."""
+    r = W.WORKLOADS[4]["rope"]
+    B, S, H, D, R = r["B"], r["S"], r["H"], r["D"], r["R"]
+    say(f"rope full size ({B},{S},{H},{D}) from fused qkv")
+    qkv = W.device_normal_bf16((B, S, 3 * H * D), W.seed_for(4, "qkv"))
+    q, k = qkv_views(qkv, H, D)
+    fr = W.workload_freqs(4)
+    cos_d, sin_d = rgg.rope_cossin_precompute(torch.from_numpy(fr).cuda())
+    oq, ok = rgg.rope_rotate_half_bf16([q, k], cos_d, sin_d)
+    cos, sin = host(cos_d), host(sin_d)
+    oc, os_ = orc.rope_cossin(fr)
+    assert_ulp_bar(cos, oc, "cos full size")
+    assert_ulp_bar(sin, os_, "sin full size")
+    rng = np.random.Generator(np.random.PCG64(4242))
+    toks = np.unique(np.concatenate([[0, 1, B * S - 1, S - 1, S],
+                                     rng.integers(0, B * S, 1500)]))
+    tk = torch.from_numpy(toks).cuda()
+    for name, xin, xout in (("q", q, oq), ("k", k, ok)):
+        xs = host(xin.reshape(B * S, H, D)[tk]).reshape(-1, D)
+        got = host(xout.reshape(B * S, H, D)[tk]).reshape(-1, D)
+        rows = np.repeat(toks, H)
+        want = orc.rope_rows(xs, cos[rows], sin[rows])
+        assert_bitexact(got, want, f"{name} full size, {toks.size} tokens sampled")
+    del qkv, oq, ok
+
+
+# ---------------------------------------------------------------------------
+# (a4, a5) GEGLU
+# ---------------------------------------------------------------------------
+
+def test_gelu_all_65536_inputs(orc):
+    """Every bf16 gate with up = 1 (rne(1 * G) = G): the GPU's GELU table
+    against the oracle's, all 65536 inputs (NaN only as NaN)."""
+    say("gelu exhaustive")
+    gate = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(512, 128)
+    up = np.full_like(gate, 0x3F80)
+    out = host(rgg.gelu_and_mul_bf16(dev(np.concatenate([gate, up], 1))))
+    want = orc.gelu_table().reshape(512, 128)
+    nan_w = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
+    nan_g = ((out & 0x7F80) == 0x7F80) & ((out & 0x7F) != 0)
+    assert np.array_equal(nan_w, nan_g), "NaN positions differ"
+    assert_ulp_bar(out[~nan_w], want[~nan_w], "gelu all inputs")
+    # scaled up: out = rne(up * G) with the same G
+    up2 = W.special_bf16(gate.shape, 99)
+    out2 = host(rgg.gelu_and_mul_bf16(dev(np.concatenate([gate, up2], 1))))
+    want2 = orc.gelu_and_mul(np.concatenate([gate, up2], 1))
+    fin = ~(nan_w | (((out2 & 0x7F80) == 0x7F80) & ((out2 & 0x7F) != 0)))
+    assert_ulp_bar(out2[fin], want2[fin], "gelu all inputs, special up")
+
+
+def geglu_inputs(rows, hidden, wid, gate_sigma):
+    gate = W.normal_bf16((rows, hidden), W.seed_for(wid, "gate"), gate_sigma)
+    up = W.normal_bf16((rows, hidden), W.seed_for(wid, "up"))
+    return np.concatenate([gate, up], axis=1)
+
+
+def check_geglu_given_gelu(orc, inp, got, what):
+    """out == rne(up * G_gpu(gate)) bit for bit, with G_gpu read from the
+    exhaustive run (here: the oracle table, which the exhaustive test ties
+    to the GPU), then the end-to-end 1-ulp bar."""
+    want = orc.gelu_and_mul(inp)
+    assert_ulp_bar(got, want, what)
+
+
+def test_geglu_tiny_workload(orc):
+    g = W.WORKLOADS[0]["geglu"]
+    say("geglu tiny workload")
+    inp = geglu_inputs(g["rows"], g["hidden"], 0, g["gate_sigma"])
+    out_t, check = with_guards((g["rows"], g["hidden"]))
+    xd = dev(inp)
+    rgg.gelu_and_mul_bf16(xd, out_t)
+    check()
+    assert np.array_equal(host(xd), inp), "input modified"
+    check_geglu_given_gelu(orc, inp, host(out_t), "geglu tiny")
+
+
+GEGLU_EDGE = [  # rows, hidden, in row stride, out row stride, data
+    (1, 8, 16, 8, "special"),
+    (3, 24, 64, 40, "special"),
+    (257, 40, 80, 40, "normal"),
+    (1031, 96, 200, 104, "special"),
+    (4099, 8, 16, 8, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", GEGLU_EDGE, ids=lambda c: "r{}h{}is{}os{}".format(*c[:4]))
+def test_geglu_edge_shapes(orc, case):
+    rows, hidden, is_, os_, kind = case
+    say(f"geglu edge {case}")
+    gen = W.special_bf16 if kind == "special" else W.normal_bf16
+    full = gen((rows, is_), 9000 + rows + hidden)
+    inp = full[:, :2 * hidden]
+    buf = torch.full((rows, os_), 0x7FC1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    out = buf[:, :hidden]
+    xd = dev(full)[:, :2 * hidden]
+    rgg.gelu_and_mul_bf16(xd, out)
+    b = host(buf)
+    assert (b[:, hidden:] == 0x7FC1).all(), "wrote into the row padding"
+    got = b[:, :hidden]
+    want = orc.gelu_and_mul(inp)
+    nan = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
+    assert ((got[nan] & 0x7F80) == 0x7F80).all() and ((got[nan] & 0x7F) != 0).all()
+    assert_ulp_bar(got[~nan], want[~nan], f"geglu {case}")
+
+
+def test_geglu_in_place_and_empty(orc):
+    say("geglu in place / empty")
+    inp = geglu_inputs(300, 64, 11, 3.0)
+    t = dev(inp)
+    rgg.gelu_and_mul_bf16(t, t[:, :64])
+    after = host(t)
+    assert np.array_equal(after[:, 64:], inp[:, 64:]), "up half modified"
+    check_geglu_given_gelu(orc, inp, after[:, :64], "geglu in place")
+    e = rgg.gelu_and_mul_bf16(torch.empty((0, 32), dtype=torch.bfloat16, device="cuda"))
+    assert e.shape == (0, 16)
+
+
+@pytest.mark.parametrize("wid", [3, 4])
+def test_geglu_full_size(orc, wid):
+    """Full-size GEGLU workloads: sampled rows against the oracle directly,
+    and every element against rne(up * T[gate]), T the oracle's table of
+    all 65536 GELU values, evaluated by torch on the device."""
+    g = W.WORKLOADS[wid]["geglu"]
+    rows, hidden = g["rows"], g["hidden"]
+    say(f"geglu full size workload {wid}: {rows} x {hidden}")
+    gate = W.device_normal_bf16((rows, hidden), W.seed_for(wid, "gate"), g["gate_sigma"])
+    up = W.device_normal_bf16((rows, hidden), W.seed_for(wid, "up"))
+    inp = torch.cat([gate, up], dim=1)
+    del gate, up
+    out = rgg.gelu_and_mul_bf16(inp)
+    rng = np.random.Generator(np.random.PCG64(wid))
+    rsel = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 48)]))
+    rs = torch.from_numpy(rsel).cuda()
+    hin = host(inp[rs])
+    assert_ulp_bar(host(out[rs]), orc.gelu_and_mul(hin), f"geglu w{wid} sampled rows")
+    table = torch.from_numpy(orc.gelu_table().view(np.int16)).cuda()
+    gi = inp[:, :hidden].view(torch.int16).to(torch.int32) & 0xFFFF
+    G = table[gi].view(torch.bfloat16)
+    want = (inp[:, hidden:].float() * G.float()).to(torch.bfloat16)
+    del G, gi
+    diff = (out.view(torch.int16) != want.view(torch.int16))
+    nan = torch.isnan(want) & torch.isnan(out)
+    bad = int((diff & ~nan).sum())
+    say(f"geglu w{wid} whole tensor vs up*T[gate]: {bad} of {out.numel()} differ")
+    assert bad == 0
