@@ -1,0 +1,319 @@
+"""Throughput of the fused RoPE + GEGLU path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dit_layer]
+
+One step = one pass of the whole path over one batch of synthetic input:
+  1. rope_cossin_precompute  angles (S, B, 1, R) fp32 -> cos/sin (B*S, R) bf16
+  2. rope_rotate_half_bf16   q and k, strided views of the fused QKV projection
+                             output (B, S, 3*H*D), one launch -> contiguous q/k
+  3. gelu_and_mul_bf16       (tokens, 2*hidden) -> (tokens, hidden)
+on the dit_layer workload (B=4, S=8192, H=32, D=128, R=128; GEGLU 32768 x
+8192), inputs drawn on the device before timing.  W untimed steps, then K
+steps between two device synchronisations; value = algorithmic bytes of a
+step / mean step time (GB/s, 1e9 bytes).  Every kernel is also bracketed by
+HIP events on the stream it runs on, which gives each one's mean launch
+duration and its algorithmic GB/s; `roofline` reports the dominant kernel.
+
+`cpu_baseline` times the CPU oracle (single thread) on a bounded sample of
+the same workload.  `roofline.traffic` comes from the committed rocprofv3
+counter summary for the dominant kernel, and is null if the kernel source has
+changed since the counters were taken.
+
+    python bench.py --pmc-summary DIR --pmc-out FILE
+turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs (DIR/fetch, DIR/write)
+into that summary; --calibration-copy adds a plain device copy of known size
+to each step so the same runs calibrate the counters.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused RoPE + GEGLU effective HBM GB/s and % of MI355X peak (bf16)"
+PEAK_HBM_GBPS = 8000.0
+KERNELS_SRC = os.path.join(ROOT, "bf16_rope_geglu_amd", "csrc", "kernels.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gelu_and_mul_dit_layer_traffic.md")
+KERNEL_SYMBOL = {
+    "precompute": "rope_cossin_kernel",
+    "rope": "rope_rotate_half_kernel",
+    "geglu": "gelu_and_mul_kernel",
+}
+COPY_BYTES = 1 << 30
+
+
+def source_digest():
+    with open(KERNELS_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# GPU benchmark
+# ---------------------------------------------------------------------------
+
+def run_gpu(args):
+    import torch
+
+    import bf16_rope_geglu_amd as rgg
+    import workloads as W
+
+    wid = {w["name"]: k for k, w in W.WORKLOADS.items()}[args.workload]
+    wl = W.WORKLOADS[wid]
+    r, g = wl["rope"], wl["geglu"]
+    B, S, H, D, R = r["B"], r["S"], r["H"], r["D"], r["R"]
+    rows, hidden = g["rows"], g["hidden"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    freqs = torch.from_numpy(W.workload_freqs(wid)).to(dev)
+    qkv = W.device_normal_bf16((B, S, 3 * H * D), W.seed_for(wid, "qkv"), device=dev)
+    q = qkv[..., :H * D].view(B, S, H, D)
+    k = qkv[..., H * D:2 * H * D].view(B, S, H, D)
+    cos = torch.empty((B * S, R), dtype=torch.bfloat16, device=dev)
+    sin = torch.empty_like(cos)
+    q_out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev)
+    k_out = torch.empty_like(q_out)
+    gate = W.device_normal_bf16((rows, hidden), W.seed_for(wid, "gate"), g["gate_sigma"], dev)
+    up = W.device_normal_bf16((rows, hidden), W.seed_for(wid, "up"), device=dev)
+    gate_up = torch.cat([gate, up], dim=1)
+    del gate, up
+    geglu_out = torch.empty((rows, hidden), dtype=torch.bfloat16, device=dev)
+    if args.calibration_copy:
+        copy_src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        copy_dst = torch.empty_like(copy_src)
+    rgg.prepare_device(0)
+    torch.cuda.synchronize()
+
+    algo = W.algo_bytes(wid)
+    step_bytes = sum(algo.values())
+    names = ["precompute", "rope", "geglu"]
+
+    def step(events=None):
+        if events:
+            events[0].record()
+        rgg.rope_cossin_precompute(freqs, cos, sin)
+        if events:
+            events[1].record()
+        rgg.rope_rotate_half_bf16([q, k], cos, sin, out=[q_out, k_out])
+        if events:
+            events[2].record()
+        rgg.gelu_and_mul_bf16(gate_up, geglu_out)
+        if events:
+            events[3].record()
+        if args.calibration_copy:
+            copy_dst.copy_(copy_src)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step throughput: K back-to-back steps, no per-kernel events
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # per-kernel launch durations: HIP events on the launch stream around each kernel
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    per = {n: 0.0 for n in names}
+    for e in evs:
+        for i, n in enumerate(names):
+            per[n] += e[i].elapsed_time(e[i + 1]) / args.steps
+    kernels = {}
+    for n in names:
+        us = per[n] * 1e3
+        gbps = algo[n] / (us * 1e-6) / 1e9
+        kernels[n] = {"symbol": KERNEL_SYMBOL[n], "us": round(us, 2), "algo_bytes": algo[n],
+                      "GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    dominant = max(names, key=lambda n: per[n])
+    return {
+        "wid": wid, "ms_per_step": ms_per_step, "wall_s": wall, "step_bytes": step_bytes,
+        "kernels": kernels, "dominant": dominant, "shape": (B, S, H, D, R, rows, hidden),
+    }
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def run_cpu_baseline(wid, tokens=4096, geglu_rows=2048):
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    o = oracle.get()
+    wl = W.WORKLOADS[wid]
+    r, g = wl["rope"], wl["geglu"]
+    H, D, R, hidden = r["H"], r["D"], r["R"], g["hidden"]
+    fr = W.workload_freqs(wid)[:tokens]             # first `tokens` positions of batch row 0
+    fr = np.ascontiguousarray(fr[:, :1])
+    q = W.normal_bf16((1, tokens, H, D), W.seed_for(wid, "q"))
+    k = W.normal_bf16((1, tokens, H, D), W.seed_for(wid, "k"))
+    gate = W.normal_bf16((geglu_rows, hidden), W.seed_for(wid, "gate"), g["gate_sigma"])
+    up = W.normal_bf16((geglu_rows, hidden), W.seed_for(wid, "up"))
+    inp = np.concatenate([gate, up], axis=1)
+
+    t0 = time.perf_counter()
+    cos, sin = o.rope_cossin(fr)
+    o.rope_rotate_half(q, cos, sin)
+    o.rope_rotate_half(k, cos, sin)
+    o.gelu_and_mul(inp)
+    dt = time.perf_counter() - t0
+    nbytes = (tokens * R * 4 + 2 * tokens * R * 2) + (2 * 2 * tokens * H * D * 2 + 2 * tokens * R * 2) \
+        + geglu_rows * hidden * 2 * 3
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {
+        "value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{tokens} of {r['B'] * r['S']} tokens (cos/sin, q and k RoPE) and "
+                   f"{geglu_rows} of {g['rows']} GEGLU rows; {nbytes} algorithmic bytes in "
+                   f"{dt:.2f} s, one thread ({affinity} cores visible)"),
+    }
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 counter summary (HBM traffic of the dominant kernel)
+# ---------------------------------------------------------------------------
+
+def _counter_rows(d):
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _per_dispatch(rows, counter, symbol):
+    vals = {}
+    for row in rows:
+        name = row.get("Kernel_Name", "")
+        if row.get("Counter_Name") != counter or symbol not in name:
+            continue
+        key = row.get("Dispatch_Id") or row.get("Correlation_Id") or str(len(vals))
+        vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    return sorted(vals.values())
+
+
+def pmc_summary(d, out):
+    fetch = _counter_rows(os.path.join(d, "fetch"))
+    write = _counter_rows(os.path.join(d, "write"))
+    copy_sym = "copy"   # torch's elementwise copy kernel name contains this
+    res = {"source_digest": source_digest(), "copy_bytes": COPY_BYTES}
+    cf = _per_dispatch(fetch, "FETCH_SIZE", copy_sym)
+    cw = _per_dispatch(write, "WRITE_SIZE", copy_sym)
+    big_f = [v for v in cf if v * 1024 > COPY_BYTES / 2]
+    big_w = [v for v in cw if v * 1024 > COPY_BYTES / 2]
+    f_scale = COPY_BYTES / (1024 * sorted(big_f)[len(big_f) // 2]) if big_f else None
+    w_scale = COPY_BYTES / (1024 * sorted(big_w)[len(big_w) // 2]) if big_w else None
+    res["fetch_scale"] = f_scale
+    res["write_scale"] = w_scale
+    lines = ["# HBM traffic per dispatch from rocprofv3 counters (dit_layer workload)", ""]
+    for n, sym in KERNEL_SYMBOL.items():
+        f = _per_dispatch(fetch, "FETCH_SIZE", sym)
+        w = _per_dispatch(write, "WRITE_SIZE", sym)
+        if not f or not w:
+            continue
+        fk, wk = f[len(f) // 2], w[len(w) // 2]
+        fb = fk * 1024 * (f_scale or 1.0)
+        wb = wk * 1024 * (w_scale or 1.0)
+        res[n] = {"fetch_kib": fk, "write_kib": wk, "bytes": fb + wb, "dispatches": len(f)}
+        lines.append(f"- {sym}: FETCH_SIZE {fk:.0f} KiB, WRITE_SIZE {wk:.0f} KiB per dispatch "
+                     f"(median of {len(f)}); scaled total {(fb + wb) / 1e9:.4f} GB")
+    lines += ["", f"Copy calibration ({COPY_BYTES} bytes each way): fetch scale {f_scale}, "
+              f"write scale {w_scale}", "", "```json", json.dumps(res, indent=1), "```", ""]
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def traffic_for(kernel):
+    """Counter bytes of `kernel` from the committed summary, if still current."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if blob.get("source_digest") != source_digest() or kernel not in blob:
+        return None
+    return blob[kernel]["bytes"]
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dit_layer", choices=["dit_layer"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true")
+    ap.add_argument("--pmc-summary", metavar="DIR")
+    ap.add_argument("--pmc-out", metavar="FILE", default=TRAFFIC_SUMMARY)
+    args = ap.parse_args()
+
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.pmc_out)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU step (each rank would run "
+              "the same per-token kernels on its own shard with no exchange); run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    res = run_gpu(args)
+    B, S, H, D, R, rows, hidden = res["shape"]
+    dom = res["dominant"]
+    kd = res["kernels"][dom]
+    traffic = traffic_for(dom)
+    value = res["step_bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 activations, 3-axis rotary angles)",
+        "config": {"workload": f"{args.workload}: fused QKV (B={B}, S={S}, 3*{H}*{D}) with q/k "
+                               f"strided views, rot_dim={R}; GEGLU {rows} x 2*{hidden}",
+                   "step_bytes": res["step_bytes"], "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": kd["symbol"], "achieved": kd["GBps"],
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": kd["frac"],
+                     "traffic": traffic},
+        "kernels": res["kernels"],
+        "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = run_cpu_baseline(res["wid"])
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -130,7 +130,7 @@ int rope_cossin_precompute(const float *freqs, int64_t S, int64_t B, int64_t R,
     if (!aligned16(freqs) || !aligned16(cos_out) || !aligned16(sin_out) || stride_s % 4 != 0 ||
         stride_b % 4 != 0)
         return RGG_ERR_ALIGN;
-    if (S * B >= kMax32 || S * B * (R / 8) >= kMax32)
+    if (S * B >= kMax32 || S * B * (R / 4) >= kMax32)
         return RGG_ERR_UNSUPPORTED;
 
     const int64_t fn[2] = {S, B}, fst[2] = {stride_s, stride_b};
@@ -230,16 +230,15 @@ int rope_rotate_half_bf16(const rgg_rope_view *views, int n_views, int64_t B, in
     p.sin = sin;
     p.tokens = B * S;
     p.n_views = n_views;
-    p.S = (int32_t)S;
     p.H = (int32_t)H;
     p.D = (int32_t)D;
     p.R = (int32_t)R;
     p.half = (int32_t)(R / 2);
-    p.tok_per_wg = rgg::rope_tokens_per_workgroup(n_views, (int)H, (int)D, (int)R);
+    p.slots_tail = (int32_t)(R / 16 + (D - R) / 8);
     p.div_s = make_fastdiv((uint32_t)S);
-    p.div_pairs = make_fastdiv(R >= 16 ? (uint32_t)(R / 16) : 1u);
     p.div_heads = make_fastdiv((uint32_t)H);
-    p.div_tail = make_fastdiv(D > R ? (uint32_t)((D - R) / 8) : 1u);
+    p.div_slots = make_fastdiv(R >= 16 ? (uint32_t)(R / 16) : 1u);
+    p.div_slots_tail = make_fastdiv((uint32_t)p.slots_tail);
     if (R == 0 && p.tail_mask == 0)
         return RGG_OK;
     return rgg::launch_rope_rotate_half(p, stream) == hipSuccess ? RGG_OK : RGG_ERR_HIP;

@@ -22,6 +22,51 @@ namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
+
+// Tunables.  The defaults are the fastest settings measured on MI355X; a
+// build may override them with -D to sweep.
+#ifndef RGG_STREAM_NT
+#define RGG_STREAM_NT 1          // nontemporal hint on data touched once
+#endif
+#ifndef RGG_GEGLU_BLOCK
+#define RGG_GEGLU_BLOCK 512      // GEGLU workgroup size
+#endif
+#ifndef RGG_GEGLU_WG_PER_CU
+#define RGG_GEGLU_WG_PER_CU 0    // 0: one vector per lane, one pass per workgroup;
+#endif                           // n: n resident workgroups per CU, grid-stride loop
+#ifndef RGG_ROPE_VEC_PER_WG
+#define RGG_ROPE_VEC_PER_WG 512  // 16-byte vectors of x per RoPE workgroup (one view)
+#endif
+#ifndef RGG_ROPE_BLOCK
+#define RGG_ROPE_BLOCK 256       // RoPE workgroup size
+#endif
+#ifndef RGG_ROPE_LDS
+#define RGG_ROPE_LDS 1           // 1: stage cos/sin rows in LDS; 0: read them per item
+#endif
+#ifndef RGG_COSSIN_COLS
+#define RGG_COSSIN_COLS 8        // table columns per lane in the cos/sin kernel (8 or 4)
+#endif
+
+// Streamed data (read or written once) bypasses cache retention when
+// RGG_STREAM_NT is set: the loads and stores carry the nontemporal bit.
+__device__ __forceinline__ v4u stream_load(const uint16_t *p)
+{
+#if RGG_STREAM_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+#else
+    return *reinterpret_cast<const v4u *>(p);
+#endif
+}
+
+__device__ __forceinline__ void stream_store(uint16_t *p, v4u v)
+{
+#if RGG_STREAM_NT
+    __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(p));
+#else
+    *reinterpret_cast<v4u *>(p) = v;
+#endif
+}
 
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f)
 {
@@ -76,7 +121,8 @@ __device__ __forceinline__ void cossin_pair(float a0, float a1, uint32_t &cw, ui
     sincosf(a1, &s1, &c1);
     cw = rne_pack(c0, c1);
     sw = rne_pack(s0, s1);
-    if (near_bf16_tie(c0) | near_bf16_tie(c1) | near_bf16_tie(s0) | near_bf16_tie(s1)) {
+    if ((int)near_bf16_tie(c0) | (int)near_bf16_tie(c1) | (int)near_bf16_tie(s0) |
+        (int)near_bf16_tie(s1)) {
         double ds0, dc0, ds1, dc1;
         sincos((double)a0, &ds0, &dc0);
         sincos((double)a1, &ds1, &dc1);
@@ -84,6 +130,8 @@ __device__ __forceinline__ void cossin_pair(float a0, float a1, uint32_t &cw, ui
         sw = bf16_from_double(ds0) | (bf16_from_double(ds1) << 16);
     }
 }
+
+constexpr int kCosSinCols = RGG_COSSIN_COLS;
 
 __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
 {
@@ -96,32 +144,44 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
         uint32_t b = fdiv(row, p.div_s);
         uint32_t s = row - b * S;
         const float4 *f = reinterpret_cast<const float4 *>(
-            p.freqs + (int64_t)s * p.stride_s + (int64_t)b * p.stride_b + cg * 8);
-        float4 f0 = f[0], f1 = f[1];
-        uint4 c, sn;
-        cossin_pair(f0.x, f0.y, c.x, sn.x);
-        cossin_pair(f0.z, f0.w, c.y, sn.y);
-        cossin_pair(f1.x, f1.y, c.z, sn.z);
-        cossin_pair(f1.z, f1.w, c.w, sn.w);
-        int64_t o = (int64_t)row * p.R + cg * 8;
-        *reinterpret_cast<uint4 *>(p.cos + o) = c;
-        *reinterpret_cast<uint4 *>(p.sin + o) = sn;
+            p.freqs + (int64_t)s * p.stride_s + (int64_t)b * p.stride_b + cg * kCosSinCols);
+        int64_t o = (int64_t)row * p.R + cg * kCosSinCols;
+        uint32_t c[kCosSinCols / 2], sn[kCosSinCols / 2];
+        float4 f0 = f[0];
+        cossin_pair(f0.x, f0.y, c[0], sn[0]);
+        cossin_pair(f0.z, f0.w, c[1], sn[1]);
+        if constexpr (kCosSinCols == 8) {
+            float4 f1 = f[1];
+            cossin_pair(f1.x, f1.y, c[2], sn[2]);
+            cossin_pair(f1.z, f1.w, c[3], sn[3]);
+            *reinterpret_cast<v4u *>(p.cos + o) = v4u{c[0], c[1], c[2], c[3]};
+            *reinterpret_cast<v4u *>(p.sin + o) = v4u{sn[0], sn[1], sn[2], sn[3]};
+        } else {
+            *reinterpret_cast<uint2 *>(p.cos + o) = make_uint2(c[0], c[1]);
+            *reinterpret_cast<uint2 *>(p.sin + o) = make_uint2(sn[0], sn[1]);
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // (a2, a3) rotate-half RoPE with tail passthrough     [ERNIE-fuse §2]
 //
-// A workgroup owns tok_per_wg consecutive tokens (table rows t0 ...).  It
-// stages their cos/sin rows in LDS once, widened to fp32, together with each
-// token's base offsets, and then every (view, head) of those tokens reuses
-// them.  Work item = (token, head, pair group p): the lane loads the 8
-// columns x[8p .. 8p+7] of the first half and x[h2+8p ..] of the second half
-// (both 16-byte vectors), rotates them against the matching 8 + 8 cos/sin
-// entries, and stores both results; each element is read and written by the
-// same lane, so out == x is safe.  Consecutive lanes take consecutive pair
-// groups and then consecutive heads, so a wave64 touches whole 128-byte
-// segments.  Two items per lane are in flight before any store.
+// A workgroup owns one view and tok_per_wg consecutive tokens (table rows
+// t0 ...); the views of the same tokens sit in neighbouring workgroups so
+// they run together and share the cos/sin rows through L2.  Work item =
+// (token, head, slot): slots 0 .. P-1 are rotation pair groups, where the
+// lane loads the 8 columns x[8p .. 8p+7] of the first half and x[h2+8p ..]
+// of the second half (two 16-byte vectors), rotates them against the
+// matching 8 + 8 cos/sin entries and stores both results; slots P .. P+Q-1
+// copy one 16-byte vector of the tail.  Consecutive lanes take consecutive
+// slots and then heads, so a wave64 requests whole head rows (and so whole
+// cache lines) at once.  Each element is read and written by one lane, so
+// out == x is safe (the tail slots are then dropped).
+//
+// The lane issues its first item's loads before the workgroup stages the
+// fp32 cos/sin rows of its tokens in LDS, so the HBM latency overlaps the
+// staging and the barrier; every (head, slot) of a token then reuses the
+// staged row.
 // ---------------------------------------------------------------------------
 
 // out1 = rne(rne(x1*c1) + rne(-x2*s1)), out2 = rne(rne(x2*c2) + rne(x1*s2)) on
@@ -140,16 +200,6 @@ __device__ __forceinline__ void rope_word(uint32_t a, uint32_t b, const float *c
     o2 = rne_pack(bf_lo(q0) + bf_hi(q0), bf_lo(q1) + bf_hi(q1));
 }
 
-__device__ __forceinline__ void rope_vec(const uint4 &x1, const uint4 &x2, const float *c1,
-                                         const float *s1, const float *c2, const float *s2,
-                                         uint4 &o1, uint4 &o2)
-{
-    rope_word(x1.x, x2.x, c1 + 0, s1 + 0, c2 + 0, s2 + 0, o1.x, o2.x);
-    rope_word(x1.y, x2.y, c1 + 2, s1 + 2, c2 + 2, s2 + 2, o1.y, o2.y);
-    rope_word(x1.z, x2.z, c1 + 4, s1 + 4, c2 + 4, s2 + 4, o1.z, o2.z);
-    rope_word(x1.w, x2.w, c1 + 6, s1 + 6, c2 + 6, s2 + 6, o1.w, o2.w);
-}
-
 __device__ __forceinline__ void load_f32x8(const float *src, float *dst)
 {
     float4 u = reinterpret_cast<const float4 *>(src)[0];
@@ -158,129 +208,144 @@ __device__ __forceinline__ void load_f32x8(const float *src, float *dst)
     dst[4] = v.x; dst[5] = v.y; dst[6] = v.z; dst[7] = v.w;
 }
 
-__global__ __launch_bounds__(kThreads) void rope_rotate_half_kernel(RopeParams p)
+// One work item located: element offsets of its x and out vectors, its
+// cos/sin offset in LDS, and whether it is a rotation item.
+struct RopeItem {
+    int64_t xo, oo;
+    int co;
+    bool rot;
+};
+
+// Token base offsets b*stride_b + s*stride_s of token t for x and out.
+__device__ __forceinline__ void rope_token_base(const RopeParams &p, const RopeView &V,
+                                                uint32_t t, int64_t &xb, int64_t &ob)
+{
+    uint32_t b = fdiv(t, p.div_s);
+    uint32_t s = t - b * p.div_s.d;
+    xb = (int64_t)b * V.xs_b + (int64_t)s * V.xs_s;
+    ob = (int64_t)b * V.os_b + (int64_t)s * V.os_s;
+}
+
+// Item i of a workgroup whose first token is t0.  With OneToken the
+// workgroup holds a single token whose base offsets xb1/ob1 are uniform.
+template <bool OneToken>
+__device__ __forceinline__ RopeItem rope_locate(const RopeParams &p, const RopeView &V,
+                                                int64_t t0, int i, int slots,
+                                                const FastDiv &div_slots, int64_t xb1,
+                                                int64_t ob1)
+{
+    const int P = p.half / 8;
+    uint32_t q = fdiv((uint32_t)i, div_slots);
+    int slot = i - (int)q * slots;
+    uint32_t tl = 0;
+    int hh = (int)q;
+    int64_t xb = xb1, ob = ob1;
+    if (!OneToken) {
+        tl = fdiv(q, p.div_heads);
+        hh = (int)q - (int)tl * p.H;
+        rope_token_base(p, V, (uint32_t)(t0 + tl), xb, ob);
+    }
+    RopeItem it;
+    it.rot = slot < P;
+    int col = it.rot ? slot * 8 : p.R + (slot - P) * 8;
+    it.xo = xb + (int64_t)hh * V.xs_h + col;
+    it.oo = ob + (int64_t)hh * V.os_h + col;
+    it.co = (int)tl * p.R + slot * 8;
+    return it;
+}
+
+constexpr int kRopeBlock = RGG_ROPE_BLOCK;
+
+__device__ __forceinline__ void load_bf16x8_as_f32(const uint16_t *src, float *dst)
+{
+    v4u w = *reinterpret_cast<const v4u *>(src);
+    dst[0] = bf_lo(w.x); dst[1] = bf_hi(w.x); dst[2] = bf_lo(w.y); dst[3] = bf_hi(w.y);
+    dst[4] = bf_lo(w.z); dst[5] = bf_hi(w.z); dst[6] = bf_lo(w.w); dst[7] = bf_hi(w.w);
+}
+
+template <bool OneToken>
+__global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int R = p.R, half = p.half, H = p.H, tpw = p.tok_per_wg;
-    float *lcos = reinterpret_cast<float *>(smem);            // [tpw][R]
-    float *lsin = lcos + tpw * R;                             // [tpw][R]
-    int64_t *lbase = reinterpret_cast<int64_t *>(lsin + tpw * R);  // [view][tok][x, out]
+    const int R = p.R, half = p.half, tpw = p.tok_per_wg;
+    float *lcos = reinterpret_cast<float *>(smem);  // [tpw][R]
+    float *lsin = lcos + tpw * R;                   // [tpw][R]
 
-    const int64_t t0 = (int64_t)blockIdx.x * tpw;
+    const uint32_t wg_tok = fdiv(blockIdx.x, p.div_views);
+    const int v = (int)(blockIdx.x - wg_tok * (uint32_t)p.n_views);
+    const int64_t t0 = (int64_t)wg_tok * tpw;
     const int ntok = (int)min((int64_t)tpw, p.tokens - t0);
+    const RopeView V = p.v[v];
+    const bool tail = (p.tail_mask >> v) & 1;
+    const int slots = tail ? p.slots_tail : p.half / 8;
+    const FastDiv div_slots = tail ? p.div_slots_tail : p.div_slots;
+    const int items = ntok * p.H * slots;
     const int tid = threadIdx.x;
+    int64_t xb1 = 0, ob1 = 0;
+    if (OneToken)
+        rope_token_base(p, V, (uint32_t)t0, xb1, ob1);
 
-    // Stage the cos/sin rows of this workgroup's tokens (consecutive rows).
+    // First item: loads in flight before the staging barrier.
+    int i = tid;
+    RopeItem it{};
+    v4u x1{}, x2{};
+    if (i < items) {
+        it = rope_locate<OneToken>(p, V, t0, i, slots, div_slots, xb1, ob1);
+        x1 = stream_load(V.x + it.xo);
+        if (it.rot)
+            x2 = stream_load(V.x + it.xo + half);
+    }
+
+#if RGG_ROPE_LDS
+    // Stage this workgroup's cos/sin rows (consecutive table rows) as fp32.
     {
-        const uint4 *gc = reinterpret_cast<const uint4 *>(p.cos + t0 * R);
-        const uint4 *gs = reinterpret_cast<const uint4 *>(p.sin + t0 * R);
+        const v4u *gc = reinterpret_cast<const v4u *>(p.cos + t0 * R);
+        const v4u *gs = reinterpret_cast<const v4u *>(p.sin + t0 * R);
         const int nvec = ntok * (R / 8);
-        for (int i = tid; i < nvec; i += kThreads) {
-            uint4 c = gc[i], s = gs[i];
-            float4 *dc = reinterpret_cast<float4 *>(lcos + i * 8);
-            float4 *ds = reinterpret_cast<float4 *>(lsin + i * 8);
+        for (int k = tid; k < nvec; k += kRopeBlock) {
+            v4u c = gc[k], sn = gs[k];
+            float4 *dc = reinterpret_cast<float4 *>(lcos + k * 8);
+            float4 *ds = reinterpret_cast<float4 *>(lsin + k * 8);
             dc[0] = make_float4(bf_lo(c.x), bf_hi(c.x), bf_lo(c.y), bf_hi(c.y));
             dc[1] = make_float4(bf_lo(c.z), bf_hi(c.z), bf_lo(c.w), bf_hi(c.w));
-            ds[0] = make_float4(bf_lo(s.x), bf_hi(s.x), bf_lo(s.y), bf_hi(s.y));
-            ds[1] = make_float4(bf_lo(s.z), bf_hi(s.z), bf_lo(s.w), bf_hi(s.w));
-        }
-    }
-    // Token base offsets per view: b*stride_b + s*stride_s for x and out.
-    for (int v = 0; v < p.n_views; ++v) {
-        const RopeView &V = p.v[v];
-        for (int tl = tid; tl < ntok; tl += kThreads) {
-            uint32_t t = (uint32_t)(t0 + tl);
-            uint32_t b = fdiv(t, p.div_s);
-            uint32_t s = t - b * p.div_s.d;
-            lbase[(v * tpw + tl) * 2 + 0] = (int64_t)b * V.xs_b + (int64_t)s * V.xs_s;
-            lbase[(v * tpw + tl) * 2 + 1] = (int64_t)b * V.os_b + (int64_t)s * V.os_s;
+            ds[0] = make_float4(bf_lo(sn.x), bf_hi(sn.x), bf_lo(sn.y), bf_hi(sn.y));
+            ds[1] = make_float4(bf_lo(sn.z), bf_hi(sn.z), bf_lo(sn.w), bf_hi(sn.w));
         }
     }
     __syncthreads();
+#endif
 
-    // Rotation: items (token, head, pair group) with the pair group fastest.
-    const int P = half / 8;
-    const int items = ntok * H * P;
-    for (int v = 0; v < p.n_views; ++v) {
-        const RopeView V = p.v[v];
-        const int64_t *vb = lbase + v * tpw * 2;
-        // item -> x offset, out offset (elements) and cos/sin offset in LDS
-        auto locate = [&](int i, int64_t &xo, int64_t &oo, int &co) {
-            uint32_t q = fdiv((uint32_t)i, p.div_pairs);
-            int pg = i - (int)q * P;
-            uint32_t tl = fdiv(q, p.div_heads);
-            int hh = (int)q - (int)tl * H;
-            xo = vb[tl * 2 + 0] + (int64_t)hh * V.xs_h + pg * 8;
-            oo = vb[tl * 2 + 1] + (int64_t)hh * V.os_h + pg * 8;
-            co = (int)tl * R + pg * 8;
-        };
-        auto rotate_store = [&](const uint4 &x1, const uint4 &x2, int64_t oo, int co) {
+    while (i < items) {
+        if (it.rot) {
             float c1[8], s1[8], c2[8], s2[8];
-            load_f32x8(lcos + co, c1);
-            load_f32x8(lsin + co, s1);
-            load_f32x8(lcos + co + half, c2);
-            load_f32x8(lsin + co + half, s2);
-            uint4 o1, o2;
-            rope_vec(x1, x2, c1, s1, c2, s2, o1, o2);
-            *reinterpret_cast<uint4 *>(V.out + oo) = o1;
-            *reinterpret_cast<uint4 *>(V.out + oo + half) = o2;
-        };
-        int i = tid;
-        // two items per lane in flight: both loads issued before either store
-        for (; i + kThreads < items; i += 2 * kThreads) {
-            int64_t xa, oa, xb, ob;
-            int ca, cb;
-            locate(i, xa, oa, ca);
-            locate(i + kThreads, xb, ob, cb);
-            uint4 a1 = *reinterpret_cast<const uint4 *>(V.x + xa);
-            uint4 a2 = *reinterpret_cast<const uint4 *>(V.x + xa + half);
-            uint4 b1 = *reinterpret_cast<const uint4 *>(V.x + xb);
-            uint4 b2 = *reinterpret_cast<const uint4 *>(V.x + xb + half);
-            rotate_store(a1, a2, oa, ca);
-            rotate_store(b1, b2, ob, cb);
+#if RGG_ROPE_LDS
+            load_f32x8(lcos + it.co, c1);
+            load_f32x8(lsin + it.co, s1);
+            load_f32x8(lcos + it.co + half, c2);
+            load_f32x8(lsin + it.co + half, s2);
+#else
+            const int64_t cg = t0 * R + it.co;
+            load_bf16x8_as_f32(p.cos + cg, c1);
+            load_bf16x8_as_f32(p.sin + cg, s1);
+            load_bf16x8_as_f32(p.cos + cg + half, c2);
+            load_bf16x8_as_f32(p.sin + cg + half, s2);
+#endif
+            uint32_t a[4], b[4];
+            rope_word(x1.x, x2.x, c1 + 0, s1 + 0, c2 + 0, s2 + 0, a[0], b[0]);
+            rope_word(x1.y, x2.y, c1 + 2, s1 + 2, c2 + 2, s2 + 2, a[1], b[1]);
+            rope_word(x1.z, x2.z, c1 + 4, s1 + 4, c2 + 4, s2 + 4, a[2], b[2]);
+            rope_word(x1.w, x2.w, c1 + 6, s1 + 6, c2 + 6, s2 + 6, a[3], b[3]);
+            stream_store(V.out + it.oo, v4u{a[0], a[1], a[2], a[3]});
+            stream_store(V.out + it.oo + half, v4u{b[0], b[1], b[2], b[3]});
+        } else {
+            stream_store(V.out + it.oo, x1);
         }
+        i += kRopeBlock;
         if (i < items) {
-            int64_t xa, oa;
-            int ca;
-            locate(i, xa, oa, ca);
-            uint4 a1 = *reinterpret_cast<const uint4 *>(V.x + xa);
-            uint4 a2 = *reinterpret_cast<const uint4 *>(V.x + xa + half);
-            rotate_store(a1, a2, oa, ca);
-        }
-    }
-
-    // Tail passthrough: columns R .. D-1, copied as bits.
-    const int Q = (p.D - R) / 8;
-    if (Q == 0)
-        return;
-    const int titems = ntok * H * Q;
-    for (int v = 0; v < p.n_views; ++v) {
-        if (!((p.tail_mask >> v) & 1))
-            continue;
-        const RopeView V = p.v[v];
-        const int64_t *vb = lbase + v * tpw * 2;
-        auto locate = [&](int i, int64_t &xo, int64_t &oo) {
-            uint32_t q = fdiv((uint32_t)i, p.div_tail);
-            int c = i - (int)q * Q;
-            uint32_t tl = fdiv(q, p.div_heads);
-            int hh = (int)q - (int)tl * H;
-            xo = vb[tl * 2 + 0] + (int64_t)hh * V.xs_h + R + c * 8;
-            oo = vb[tl * 2 + 1] + (int64_t)hh * V.os_h + R + c * 8;
-        };
-        int i = tid;
-        for (; i + kThreads < titems; i += 2 * kThreads) {
-            int64_t xa, oa, xb, ob;
-            locate(i, xa, oa);
-            locate(i + kThreads, xb, ob);
-            uint4 a = *reinterpret_cast<const uint4 *>(V.x + xa);
-            uint4 b = *reinterpret_cast<const uint4 *>(V.x + xb);
-            *reinterpret_cast<uint4 *>(V.out + oa) = a;
-            *reinterpret_cast<uint4 *>(V.out + ob) = b;
-        }
-        if (i < titems) {
-            int64_t xa, oa;
-            locate(i, xa, oa);
-            *reinterpret_cast<uint4 *>(V.out + oa) = *reinterpret_cast<const uint4 *>(V.x + xa);
+            it = rope_locate<OneToken>(p, V, t0, i, slots, div_slots, xb1, ob1);
+            x1 = stream_load(V.x + it.xo);
+            if (it.rot)
+                x2 = stream_load(V.x + it.xo + half);
         }
     }
 }
@@ -299,9 +364,13 @@ __global__ __launch_bounds__(kThreads) void rope_rotate_half_kernel(RopeParams p
 //                         x/2 rounds toward +inf;
 //   x >= 16: G = x;  x <= -16: G = -0 (|G| < 1e-56);  G(+inf) = +inf,
 //   G(-inf) = NaN, NaN -> NaN.
-// Inputs outside [2^-125, 16) in magnitude are rare, so a wave takes the
-// general path only when one of its lanes holds one.  The multiply by up is
-// exact in fp32 and rounded once.
+// The common path (|x| in [2^-125, 16)) is branch-free; a vector holding an
+// input outside it (rare: |x| < 2^-125 or >= 16) is redone by the general
+// path.  The multiply by up is exact in fp32 and rounded once.
+//
+// Layout of the work: one 16-byte vector (8 outputs) per lane.  The lane
+// issues its gate and up loads, then the workgroup copies the table into
+// LDS, so the table fill overlaps the HBM latency.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kLutLo = 0x3A80u;                // bf16 bits of 2^-10
 constexpr uint32_t kLutHi = 0x4180u;                // bf16 bits of 16.0
@@ -322,16 +391,16 @@ __global__ __launch_bounds__(kThreads) void build_gelu_table_kernel()
     g_gelu_lut[i] = (uint16_t)bf16_from_double(g);
 }
 
-// G for a bf16 gate whose magnitude is in [2^-125, 16).
+// G, as fp32 bits, for a bf16 gate whose magnitude is in [2^-125, 16).
 __device__ __forceinline__ uint32_t gelu_common(uint32_t g, const uint16_t *lut)
 {
     uint32_t a = g & 0x7FFFu;
     uint32_t idx = max(a, kLutLo) - kLutLo + (g >> 15) * kLutSpan;
     uint32_t t = lut[idx];
-    return a < kLutLo ? g - 0x80u : t;
+    return (a < kLutLo ? g - 0x80u : t) << 16;
 }
 
-// G for any bf16 gate.
+// G, as bf16 bits, for any bf16 gate.
 __device__ uint32_t gelu_general(uint32_t g, const uint16_t *lut)
 {
     uint32_t a = g & 0x7FFFu;
@@ -343,7 +412,7 @@ __device__ uint32_t gelu_general(uint32_t g, const uint16_t *lut)
     if (a >= kLutHi)
         return neg ? 0x8000u : g;
     if (a >= 0x0100u)
-        return gelu_common(g, lut);
+        return gelu_common(g, lut) >> 16;
     return neg ? (0x8000u | (a >> 1)) : ((a + 1u) >> 1);
 }
 
@@ -355,61 +424,68 @@ __device__ __forceinline__ bool word_needs_general(uint32_t w)
     return max(lo, hi) >= kLutHi - 0x0100u;
 }
 
-__device__ __forceinline__ uint32_t geglu_word(uint32_t gw, uint32_t uw, const uint16_t *lut,
-                                               bool general)
+__device__ __forceinline__ uint32_t geglu_word_common(uint32_t gw, uint32_t uw,
+                                                      const uint16_t *lut)
 {
-    uint32_t g0, g1;
-    if (general) {
-        g0 = gelu_general(gw & 0xFFFFu, lut);
-        g1 = gelu_general(gw >> 16, lut);
-    } else {
-        g0 = gelu_common(gw & 0xFFFFu, lut);
-        g1 = gelu_common(gw >> 16, lut);
-    }
-    return rne_pack(bf_lo(uw) * __uint_as_float(g0 << 16), bf_hi(uw) * __uint_as_float(g1 << 16));
+    float g0 = __uint_as_float(gelu_common(gw & 0xFFFFu, lut));
+    float g1 = __uint_as_float(gelu_common(gw >> 16, lut));
+    return rne_pack(bf_lo(uw) * g0, bf_hi(uw) * g1);
 }
 
-constexpr int kGegluUnroll = 4;
+__device__ __noinline__ v4u geglu_vec_general(v4u g, v4u u, const uint16_t *lut)
+{
+    uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w}, o[4];
+    for (int k = 0; k < 4; ++k) {
+        float g0 = __uint_as_float(gelu_general(gw[k] & 0xFFFFu, lut) << 16);
+        float g1 = __uint_as_float(gelu_general(gw[k] >> 16, lut) << 16);
+        o[k] = rne_pack(bf_lo(uw[k]) * g0, bf_hi(uw[k]) * g1);
+    }
+    return v4u{o[0], o[1], o[2], o[3]};
+}
 
-__global__ __launch_bounds__(kThreads) void gelu_and_mul_kernel(GegluParams p)
+__device__ __forceinline__ v4u geglu_vec(v4u g, v4u u, const uint16_t *lut)
+{
+    v4u o = v4u{geglu_word_common(g.x, u.x, lut), geglu_word_common(g.y, u.y, lut),
+                geglu_word_common(g.z, u.z, lut), geglu_word_common(g.w, u.w, lut)};
+    bool general = (int)word_needs_general(g.x) | (int)word_needs_general(g.y) |
+                   (int)word_needs_general(g.z) | (int)word_needs_general(g.w);
+    if (general)
+        o = geglu_vec_general(g, u, lut);
+    return o;
+}
+
+constexpr int kGegluBlock = RGG_GEGLU_BLOCK;
+
+__global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p)
 {
     __shared__ __align__(16) uint16_t lut[kLutEntries];
-    for (uint32_t i = threadIdx.x; i < kLutEntries / 8; i += kThreads)
-        reinterpret_cast<uint4 *>(lut)[i] = reinterpret_cast<const uint4 *>(g_gelu_lut)[i];
+    const uint32_t nvec_row = p.div_vecs.d;
+    const uint32_t step = gridDim.x * kGegluBlock;
+    uint32_t idx = blockIdx.x * kGegluBlock + threadIdx.x;
+
+    v4u g{}, u{};
+    int64_t oo = 0;
+    auto fetch = [&](uint32_t j) {
+        uint32_t row = fdiv(j, p.div_vecs);
+        uint32_t col = (j - row * nvec_row) * 8;
+        const uint16_t *src = p.in + (int64_t)row * p.in_stride + col;
+        g = stream_load(src);
+        u = stream_load(src + p.hidden);
+        oo = (int64_t)row * p.out_stride + col;
+    };
+    if (idx < p.vec_total)
+        fetch(idx);
+
+    for (uint32_t k = threadIdx.x; k < kLutEntries / 8; k += kGegluBlock)
+        reinterpret_cast<v4u *>(lut)[k] = reinterpret_cast<const v4u *>(g_gelu_lut)[k];
     __syncthreads();
 
-    const uint32_t nvec_row = p.div_vecs.d;
-    const uint32_t step = gridDim.x * (kThreads * kGegluUnroll);
-    for (uint32_t base = blockIdx.x * (kThreads * kGegluUnroll); base < p.vec_total;
-         base += step) {
-        uint4 g[kGegluUnroll], u[kGegluUnroll];
-        int64_t oo[kGegluUnroll];
-#pragma unroll
-        for (int k = 0; k < kGegluUnroll; ++k) {
-            uint32_t idx = base + k * kThreads + threadIdx.x;
-            if (idx < p.vec_total) {
-                uint32_t row = fdiv(idx, p.div_vecs);
-                uint32_t col = (idx - row * nvec_row) * 8;
-                const uint16_t *src = p.in + (int64_t)row * p.in_stride + col;
-                g[k] = *reinterpret_cast<const uint4 *>(src);
-                u[k] = *reinterpret_cast<const uint4 *>(src + p.hidden);
-                oo[k] = (int64_t)row * p.out_stride + col;
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kGegluUnroll; ++k) {
-            uint32_t idx = base + k * kThreads + threadIdx.x;
-            if (idx < p.vec_total) {
-                bool general = word_needs_general(g[k].x) | word_needs_general(g[k].y) |
-                               word_needs_general(g[k].z) | word_needs_general(g[k].w);
-                uint4 o;
-                o.x = geglu_word(g[k].x, u[k].x, lut, general);
-                o.y = geglu_word(g[k].y, u[k].y, lut, general);
-                o.z = geglu_word(g[k].z, u[k].z, lut, general);
-                o.w = geglu_word(g[k].w, u[k].w, lut, general);
-                *reinterpret_cast<uint4 *>(p.out + oo[k]) = o;
-            }
-        }
+    while (idx < p.vec_total) {
+        v4u o = geglu_vec(g, u, lut);
+        stream_store(p.out + oo, o);
+        idx += step;
+        if (idx < p.vec_total)
+            fetch(idx);
     }
 }
 
@@ -418,8 +494,12 @@ __global__ __launch_bounds__(kThreads) void gelu_and_mul_kernel(GegluParams p)
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_rope_cossin(const CosSinParams &p, hipStream_t stream)
+hipError_t launch_rope_cossin(const CosSinParams &params, hipStream_t stream)
 {
+    CosSinParams p = params;
+    uint32_t rows = p.vec_total / (uint32_t)(p.R / 8);
+    p.vec_total = rows * (uint32_t)(p.R / kCosSinCols);
+    p.div_vecs = make_fastdiv((uint32_t)(p.R / kCosSinCols));
     uint32_t blocks = (p.vec_total + kThreads - 1) / kThreads;
     if (blocks > 4096)
         blocks = 4096;
@@ -427,19 +507,25 @@ hipError_t launch_rope_cossin(const CosSinParams &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_rope_rotate_half(const RopeParams &p, hipStream_t stream)
+hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
 {
-    int64_t blocks = (p.tokens + p.tok_per_wg - 1) / p.tok_per_wg;
-    size_t lds = (size_t)p.tok_per_wg * p.R * 2 * sizeof(float) +
-                 (size_t)p.n_views * p.tok_per_wg * 2 * sizeof(int64_t);
-    hipLaunchKernelGGL(rope_rotate_half_kernel, dim3((uint32_t)blocks), dim3(kThreads), lds,
-                       stream, p);
+    RopeParams p = params;
+    p.tok_per_wg = rope_tokens_per_workgroup(p.H, p.D, p.R);
+    p.div_views = make_fastdiv((uint32_t)p.n_views);
+    int64_t blocks = (p.tokens + p.tok_per_wg - 1) / p.tok_per_wg * p.n_views;
+    size_t lds = RGG_ROPE_LDS ? (size_t)p.tok_per_wg * p.R * 2 * sizeof(float) : 0;
+    if (p.tok_per_wg == 1)
+        hipLaunchKernelGGL(rope_rotate_half_kernel<true>, dim3((uint32_t)blocks), dim3(kRopeBlock),
+                           lds, stream, p);
+    else
+        hipLaunchKernelGGL(rope_rotate_half_kernel<false>, dim3((uint32_t)blocks),
+                           dim3(kRopeBlock), lds, stream, p);
     return hipGetLastError();
 }
 
 hipError_t launch_gelu_and_mul(const GegluParams &p, int grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL(gelu_and_mul_kernel, dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(gelu_and_mul_kernel, dim3(grid), dim3(kGegluBlock), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -450,29 +536,33 @@ hipError_t launch_build_gelu_table(hipStream_t stream)
     return hipGetLastError();
 }
 
-int rope_tokens_per_workgroup(int n_views, int H, int D, int R)
+int rope_tokens_per_workgroup(int H, int D, int R)
 {
-    // About 4096 16-byte vectors (64 KiB) of x per workgroup, and the LDS
-    // staging (fp32 cos/sin rows plus two offsets per view) within 32 KiB.
-    int64_t vec_per_tok = (int64_t)n_views * H * (D / 8);
-    int64_t t = vec_per_tok > 0 ? 4096 / vec_per_tok : 64;
+    // About RGG_ROPE_VEC_PER_WG 16-byte vectors of x per workgroup, with the
+    // fp32 cos/sin staging within 32 KiB of LDS.
+    int64_t vec_per_tok = (int64_t)H * (D / 8);
+    int64_t t = vec_per_tok > 0 ? RGG_ROPE_VEC_PER_WG / vec_per_tok : 64;
     if (t < 1)
         t = 1;
     if (t > 64)
         t = 64;
-    while (t > 1 && t * R * 8 + t * n_views * 16 > 32768)
+    while (t > 1 && t * R * 8 > 32768)
         --t;
     return (int)t;
 }
 
 int geglu_grid(uint32_t vec_total, int cu_count)
 {
-    // Persistent: up to 8 workgroups per compute unit, each looping over
-    // chunks of kThreads * kGegluUnroll vectors (the LUT is loaded once per
-    // workgroup).
-    uint32_t chunks = (vec_total + kThreads * kGegluUnroll - 1) / (kThreads * kGegluUnroll);
-    uint32_t cap = (uint32_t)(cu_count > 0 ? cu_count : 256) * 8;
-    return (int)(chunks < cap ? (chunks > 0 ? chunks : 1) : cap);
+    // One vector per lane; with RGG_GEGLU_WG_PER_CU > 0 the grid is capped at
+    // that many workgroups per compute unit and each loops (grid stride).
+    const uint32_t chunk = kGegluBlock;
+    uint32_t chunks = (vec_total + chunk - 1) / chunk;
+    if (chunks == 0)
+        chunks = 1;
+    if (RGG_GEGLU_WG_PER_CU == 0)
+        return (int)chunks;
+    uint32_t cap = (uint32_t)(cu_count > 0 ? cu_count : 256) * RGG_GEGLU_WG_PER_CU;
+    return (int)(chunks < cap ? chunks : cap);
 }
 
 }  // namespace rgg

@@ -41,15 +41,16 @@ struct RopeParams {
     const uint16_t *sin;
     int64_t tokens;        // B * S
     int32_t n_views;
-    int32_t S;             // only used through div_s
     int32_t H, D, R;
     int32_t half;          // R / 2
-    int32_t tok_per_wg;    // tokens handled by one workgroup
+    int32_t tok_per_wg;    // tokens handled by one workgroup (of one view)
     int32_t tail_mask;     // bit v set: copy the tail of view v
+    int32_t slots_tail;    // R/16 + (D - R)/8 work slots per head when the tail is copied
     FastDiv div_s;         // token -> (b, s)
-    FastDiv div_pairs;     // rotation item -> (token-local, head, pair); divisor R/16
+    FastDiv div_views;     // workgroup -> (token chunk, view)
     FastDiv div_heads;     // divisor H
-    FastDiv div_tail;      // divisor (D - R) / 8
+    FastDiv div_slots;     // divisor R/16: item -> (token-local, head, slot), no tail
+    FastDiv div_slots_tail;  // divisor slots_tail
 };
 
 struct CosSinParams {
@@ -79,7 +80,7 @@ hipError_t launch_gelu_and_mul(const GegluParams &p, int grid, hipStream_t strea
 hipError_t launch_build_gelu_table(hipStream_t stream);
 
 // Tunables chosen by the host layer.
-int rope_tokens_per_workgroup(int n_views, int H, int D, int R);
+int rope_tokens_per_workgroup(int H, int D, int R);
 int geglu_grid(uint32_t vec_total, int cu_count);
 
 }  // namespace rgg
