@@ -149,6 +149,97 @@ def run_gpu(args):
 
 
 # ---------------------------------------------------------------------------
+# per-kernel sweep over every workload, cold caches
+# ---------------------------------------------------------------------------
+
+def run_sweep(reps=40, touch=2 << 30):
+    """Per-launch time of each kernel on each workload.  Enough input and
+    output sets are allocated that consecutive launches touch `touch` bytes
+    (well past the 256 MB Infinity Cache) and launches rotate through them, so
+    every launch streams from HBM.  `reps` launches are captured in one HIP
+    graph and replayed between two events, so host launch overhead does not
+    pad the short kernels."""
+    import torch
+
+    import bf16_rope_geglu_amd as rgg
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rgg.prepare_device(0)
+    rows_out = []
+
+    def timed(fns, nbytes):
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for r in range(reps):
+                fns[r % len(fns)]()
+        graph.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        del graph
+        return us, nbytes / (us * 1e-6) / 1e9
+
+    for wid, wl in sorted(W.WORKLOADS.items()):
+        if wid == 0:
+            continue
+        algo = W.algo_bytes(wid)
+        if "rope" in wl:
+            r = wl["rope"]
+            B, S, H, D, R = r["B"], r["S"], r["H"], r["D"], r["R"]
+            nsets = max(2, -(-touch // (algo["rope"] + algo["precompute"])))
+            fr = torch.from_numpy(W.workload_freqs(wid)).to(dev)
+            sets = []
+            for k in range(nsets):
+                freqs = fr.clone()
+                cos, sin = rgg.rope_cossin_precompute(freqs)
+                if r["layout"] == "qkv":
+                    qkv = W.device_normal_bf16((B, S, 3 * H * D), 100 + k, device=dev)
+                    xs = [qkv[..., :H * D].view(B, S, H, D), qkv[..., H * D:2 * H * D].view(B, S, H, D)]
+                else:
+                    xs = [W.device_normal_bf16((B, S, H, D), 100 + 4 * k + v, device=dev)
+                          for v in range(r["views"])]
+                outs = [torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev) for _ in xs]
+                sets.append((freqs, cos, sin, xs, outs))
+            pre = [(lambda st=st: rgg.rope_cossin_precompute(st[0], st[1], st[2])) for st in sets]
+            rot = [(lambda st=st: rgg.rope_rotate_half_bf16(st[3], st[1], st[2], out=st[4]))
+                   for st in sets]
+            for name, fns in (("rope_cossin_precompute", pre), ("rope_rotate_half_bf16", rot)):
+                key = "precompute" if "cossin" in name else "rope"
+                us, gbps = timed(fns, algo[key])
+                rows_out.append((wl["name"], name, algo[key], nsets, us, gbps))
+            del sets
+        if "geglu" in wl:
+            g = wl["geglu"]
+            nsets = max(2, -(-touch // algo["geglu"]))
+            sets = []
+            for k in range(nsets):
+                inp = W.device_normal_bf16((g["rows"], 2 * g["hidden"]), 200 + k, g["gate_sigma"], dev)
+                out = torch.empty((g["rows"], g["hidden"]), dtype=torch.bfloat16, device=dev)
+                sets.append((inp, out))
+            fns = [(lambda st=st: rgg.gelu_and_mul_bf16(st[0], st[1])) for st in sets]
+            us, gbps = timed(fns, algo["geglu"])
+            rows_out.append((wl["name"], "gelu_and_mul_bf16", algo["geglu"], nsets, us, gbps))
+            del sets
+        torch.cuda.empty_cache()
+
+    print("| workload | entry point | algorithmic bytes | buffer sets | us per launch | GB/s | % of 8 TB/s |")
+    print("|---|---|---|---|---|---|---|")
+    for w, n, b, k, us, gbps in rows_out:
+        print(f"| {w} | {n} | {b} | {k} | {us:.1f} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f} |")
+    sys.stdout.flush()
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
 
@@ -213,10 +304,36 @@ def _per_dispatch(rows, counter, symbol):
     return sorted(vals.values())
 
 
-def pmc_summary(d, out):
+def trace_summary(d, out, command):
+    """Short markdown table of a rocprofv3 --kernel-trace --stats run."""
+    paths = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    rows = []
+    for path in paths:
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    lines = ["# rocprofv3 kernel trace, dit_layer workload", "",
+             f"Command: `{command}`", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for row in rows:
+        name = row["Name"]
+        short = next((v for v in KERNEL_SYMBOL.values() if v in name), None)
+        if short is None and "gelu_table" not in name:
+            continue
+        short = short or "build_gelu_table_kernel"
+        lines.append(f"| {short} | {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | "
+                     f"{float(row['MinNs']) / 1e3:.2f} | {float(row['MaxNs']) / 1e3:.2f} |")
+    lines.append("")
+    text = "\n".join(lines)
+    if out:
+        with open(out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def pmc_summary(d, out, command=""):
     fetch = _counter_rows(os.path.join(d, "fetch"))
     write = _counter_rows(os.path.join(d, "write"))
-    copy_sym = "copy"   # torch's elementwise copy kernel name contains this
+    copy_sym = "copyBuffer"   # the HIP runtime's device-to-device copy kernel
     res = {"source_digest": source_digest(), "copy_bytes": COPY_BYTES}
     cf = _per_dispatch(fetch, "FETCH_SIZE", copy_sym)
     cw = _per_dispatch(write, "WRITE_SIZE", copy_sym)
@@ -226,7 +343,8 @@ def pmc_summary(d, out):
     w_scale = COPY_BYTES / (1024 * sorted(big_w)[len(big_w) // 2]) if big_w else None
     res["fetch_scale"] = f_scale
     res["write_scale"] = w_scale
-    lines = ["# HBM traffic per dispatch from rocprofv3 counters (dit_layer workload)", ""]
+    lines = ["# HBM traffic per dispatch from rocprofv3 counters (dit_layer workload)", "",
+             f"Commands: `{command}`", ""]
     for n, sym in KERNEL_SYMBOL.items():
         f = _per_dispatch(fetch, "FETCH_SIZE", sym)
         w = _per_dispatch(write, "WRITE_SIZE", sym)
@@ -270,10 +388,21 @@ def main():
     ap.add_argument("--calibration-copy", action="store_true")
     ap.add_argument("--pmc-summary", metavar="DIR")
     ap.add_argument("--pmc-out", metavar="FILE", default=TRAFFIC_SUMMARY)
+    ap.add_argument("--trace-summary", metavar="DIR")
+    ap.add_argument("--trace-out", metavar="FILE")
+    ap.add_argument("--command", default="", help="command line recorded in summaries")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every kernel on every workload (cold caches) instead")
     args = ap.parse_args()
 
     if args.pmc_summary:
-        pmc_summary(args.pmc_summary, args.pmc_out)
+        pmc_summary(args.pmc_summary, args.pmc_out, args.command)
+        return 0
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.trace_out, args.command)
+        return 0
+    if args.sweep:
+        run_sweep()
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU step (each rank would run "

@@ -68,6 +68,27 @@ __device__ __forceinline__ void stream_store(uint16_t *p, v4u v)
 #endif
 }
 
+// Load/store whose nontemporal hint is chosen per launch: the hint pays only
+// when every 128-byte line is read or written whole by one instruction;
+// lines split between instructions are better merged in L2 first.
+template <bool Nt>
+__device__ __forceinline__ v4u load16(const uint16_t *p)
+{
+    if constexpr (Nt)
+        return stream_load(p);
+    else
+        return *reinterpret_cast<const v4u *>(p);
+}
+
+template <bool Nt>
+__device__ __forceinline__ void store16(uint16_t *p, v4u v)
+{
+    if constexpr (Nt)
+        stream_store(p, v);
+    else
+        *reinterpret_cast<v4u *>(p) = v;
+}
+
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f)
 {
     return (__umulhi(n, f.m) + n) >> f.l;
@@ -100,13 +121,18 @@ __device__ __forceinline__ uint32_t bf16_from_double(double v)
 // (a1) cos/sin tables                             [ERNIE-fuse §1]
 //
 // One lane per 8 consecutive rotary columns of one table row: two 16-byte
-// angle loads, eight fp32 sincosf, two 16-byte stores.  An fp32 result whose
-// low 16 bits lie within kTieGuard units of 0x8000 is too close to a bf16
-// rounding midpoint for fp32's few-ulp error to decide; those (about one in
-// a thousand) are recomputed in double and rounded exactly, so each entry is
-// the correctly rounded bf16 of cos/sin of the fp32 angle.
+// angle loads, eight fp32 sincosf, two 16-byte stores.  sincosf is accurate
+// to a couple of fp32 ulps, so rounding its result to bf16 gives the
+// correctly rounded bf16 of the true value unless the fp32 result lies within
+// a few ulps of a bf16 rounding midpoint (its low 16 bits near 0x8000).
+// Those few (about one in 7000) are recomputed in double and rounded exactly,
+// so each entry is the correctly rounded bf16 of cos/sin of the fp32 angle.
+// RGG_COSSIN_GUARD is that margin in fp32 ulps.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kTieGuard = 64;
+#ifndef RGG_COSSIN_GUARD
+#define RGG_COSSIN_GUARD 4
+#endif
+constexpr uint32_t kTieGuard = RGG_COSSIN_GUARD;
 
 __device__ __forceinline__ bool near_bf16_tie(float r)
 {
@@ -133,32 +159,68 @@ __device__ __forceinline__ void cossin_pair(float a0, float a1, uint32_t &cw, ui
 
 constexpr int kCosSinCols = RGG_COSSIN_COLS;
 
+__device__ __forceinline__ void cossin_vec8(v4u a0, v4u a1, uint32_t *c, uint32_t *sn)
+{
+    cossin_pair(__uint_as_float(a0.x), __uint_as_float(a0.y), c[0], sn[0]);
+    cossin_pair(__uint_as_float(a0.z), __uint_as_float(a0.w), c[1], sn[1]);
+    cossin_pair(__uint_as_float(a1.x), __uint_as_float(a1.y), c[2], sn[2]);
+    cossin_pair(__uint_as_float(a1.z), __uint_as_float(a1.w), c[3], sn[3]);
+}
+
+// Paired form (R a multiple of 16): a lane owns columns 8g .. 8g+7 of both
+// halves of a row.  Rotate-half angle tables usually repeat the first half
+// in the second (cat(f, f)); when the eight angles of the second half are
+// bitwise the first half's, their cos/sin are reused instead of recomputed.
+template <bool Paired>
 __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
 {
     const uint32_t nvec_row = p.div_vecs.d;
     const uint32_t S = p.div_s.d;
+    const int half = p.R / 2;
     for (uint32_t idx = blockIdx.x * kThreads + threadIdx.x; idx < p.vec_total;
          idx += gridDim.x * kThreads) {
         uint32_t row = fdiv(idx, p.div_vecs);
         uint32_t cg = idx - row * nvec_row;
         uint32_t b = fdiv(row, p.div_s);
         uint32_t s = row - b * S;
-        const float4 *f = reinterpret_cast<const float4 *>(
-            p.freqs + (int64_t)s * p.stride_s + (int64_t)b * p.stride_b + cg * kCosSinCols);
-        int64_t o = (int64_t)row * p.R + cg * kCosSinCols;
-        uint32_t c[kCosSinCols / 2], sn[kCosSinCols / 2];
-        float4 f0 = f[0];
-        cossin_pair(f0.x, f0.y, c[0], sn[0]);
-        cossin_pair(f0.z, f0.w, c[1], sn[1]);
-        if constexpr (kCosSinCols == 8) {
-            float4 f1 = f[1];
-            cossin_pair(f1.x, f1.y, c[2], sn[2]);
-            cossin_pair(f1.z, f1.w, c[3], sn[3]);
-            *reinterpret_cast<v4u *>(p.cos + o) = v4u{c[0], c[1], c[2], c[3]};
-            *reinterpret_cast<v4u *>(p.sin + o) = v4u{sn[0], sn[1], sn[2], sn[3]};
+        const float *f = p.freqs + (int64_t)s * p.stride_s + (int64_t)b * p.stride_b;
+        int64_t o = (int64_t)row * p.R;
+        if constexpr (Paired) {
+            const int col = cg * 8;
+            uint32_t c[4], sn[4];
+            v4u a0 = *reinterpret_cast<const v4u *>(f + col);
+            v4u a1 = *reinterpret_cast<const v4u *>(f + col + 4);
+            v4u b0 = *reinterpret_cast<const v4u *>(f + half + col);
+            v4u b1 = *reinterpret_cast<const v4u *>(f + half + col + 4);
+            cossin_vec8(a0, a1, c, sn);
+            v4u cv = v4u{c[0], c[1], c[2], c[3]}, sv = v4u{sn[0], sn[1], sn[2], sn[3]};
+            *reinterpret_cast<v4u *>(p.cos + o + col) = cv;
+            *reinterpret_cast<v4u *>(p.sin + o + col) = sv;
+            bool same = a0.x == b0.x && a0.y == b0.y && a0.z == b0.z && a0.w == b0.w &&
+                        a1.x == b1.x && a1.y == b1.y && a1.z == b1.z && a1.w == b1.w;
+            if (!same) {
+                cossin_vec8(b0, b1, c, sn);
+                cv = v4u{c[0], c[1], c[2], c[3]};
+                sv = v4u{sn[0], sn[1], sn[2], sn[3]};
+            }
+            *reinterpret_cast<v4u *>(p.cos + o + half + col) = cv;
+            *reinterpret_cast<v4u *>(p.sin + o + half + col) = sv;
         } else {
-            *reinterpret_cast<uint2 *>(p.cos + o) = make_uint2(c[0], c[1]);
-            *reinterpret_cast<uint2 *>(p.sin + o) = make_uint2(sn[0], sn[1]);
+            const int col = cg * kCosSinCols;
+            uint32_t c[kCosSinCols / 2], sn[kCosSinCols / 2];
+            float4 f0 = reinterpret_cast<const float4 *>(f + col)[0];
+            cossin_pair(f0.x, f0.y, c[0], sn[0]);
+            cossin_pair(f0.z, f0.w, c[1], sn[1]);
+            if constexpr (kCosSinCols == 8) {
+                float4 f1 = reinterpret_cast<const float4 *>(f + col)[1];
+                cossin_pair(f1.x, f1.y, c[2], sn[2]);
+                cossin_pair(f1.z, f1.w, c[3], sn[3]);
+                *reinterpret_cast<v4u *>(p.cos + o + col) = v4u{c[0], c[1], c[2], c[3]};
+                *reinterpret_cast<v4u *>(p.sin + o + col) = v4u{sn[0], sn[1], sn[2], sn[3]};
+            } else {
+                *reinterpret_cast<uint2 *>(p.cos + o + col) = make_uint2(c[0], c[1]);
+                *reinterpret_cast<uint2 *>(p.sin + o + col) = make_uint2(sn[0], sn[1]);
+            }
         }
     }
 }
@@ -263,7 +325,7 @@ __device__ __forceinline__ void load_bf16x8_as_f32(const uint16_t *src, float *d
     dst[4] = bf_lo(w.z); dst[5] = bf_hi(w.z); dst[6] = bf_lo(w.w); dst[7] = bf_hi(w.w);
 }
 
-template <bool OneToken>
+template <bool OneToken, bool Nt>
 __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -291,9 +353,9 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
     v4u x1{}, x2{};
     if (i < items) {
         it = rope_locate<OneToken>(p, V, t0, i, slots, div_slots, xb1, ob1);
-        x1 = stream_load(V.x + it.xo);
+        x1 = load16<Nt>(V.x + it.xo);
         if (it.rot)
-            x2 = stream_load(V.x + it.xo + half);
+            x2 = load16<Nt>(V.x + it.xo + half);
     }
 
 #if RGG_ROPE_LDS
@@ -335,17 +397,17 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
             rope_word(x1.y, x2.y, c1 + 2, s1 + 2, c2 + 2, s2 + 2, a[1], b[1]);
             rope_word(x1.z, x2.z, c1 + 4, s1 + 4, c2 + 4, s2 + 4, a[2], b[2]);
             rope_word(x1.w, x2.w, c1 + 6, s1 + 6, c2 + 6, s2 + 6, a[3], b[3]);
-            stream_store(V.out + it.oo, v4u{a[0], a[1], a[2], a[3]});
-            stream_store(V.out + it.oo + half, v4u{b[0], b[1], b[2], b[3]});
+            store16<Nt>(V.out + it.oo, v4u{a[0], a[1], a[2], a[3]});
+            store16<Nt>(V.out + it.oo + half, v4u{b[0], b[1], b[2], b[3]});
         } else {
-            stream_store(V.out + it.oo, x1);
+            store16<Nt>(V.out + it.oo, x1);
         }
         i += kRopeBlock;
         if (i < items) {
             it = rope_locate<OneToken>(p, V, t0, i, slots, div_slots, xb1, ob1);
-            x1 = stream_load(V.x + it.xo);
+            x1 = load16<Nt>(V.x + it.xo);
             if (it.rot)
-                x2 = stream_load(V.x + it.xo + half);
+                x2 = load16<Nt>(V.x + it.xo + half);
         }
     }
 }
@@ -497,13 +559,18 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
 hipError_t launch_rope_cossin(const CosSinParams &params, hipStream_t stream)
 {
     CosSinParams p = params;
-    uint32_t rows = p.vec_total / (uint32_t)(p.R / 8);
-    p.vec_total = rows * (uint32_t)(p.R / kCosSinCols);
-    p.div_vecs = make_fastdiv((uint32_t)(p.R / kCosSinCols));
+    const uint32_t rows = p.vec_total / (uint32_t)(p.R / 8);
+    const bool paired = p.R % 16 == 0;
+    const uint32_t per_row = paired ? (uint32_t)(p.R / 16) : (uint32_t)(p.R / kCosSinCols);
+    p.vec_total = rows * per_row;
+    p.div_vecs = make_fastdiv(per_row);
     uint32_t blocks = (p.vec_total + kThreads - 1) / kThreads;
     if (blocks > 4096)
         blocks = 4096;
-    hipLaunchKernelGGL(rope_cossin_kernel, dim3(blocks), dim3(kThreads), 0, stream, p);
+    if (paired)
+        hipLaunchKernelGGL(rope_cossin_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(rope_cossin_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -514,12 +581,23 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
     p.div_views = make_fastdiv((uint32_t)p.n_views);
     int64_t blocks = (p.tokens + p.tok_per_wg - 1) / p.tok_per_wg * p.n_views;
     size_t lds = RGG_ROPE_LDS ? (size_t)p.tok_per_wg * p.R * 2 * sizeof(float) : 0;
-    if (p.tok_per_wg == 1)
-        hipLaunchKernelGGL(rope_rotate_half_kernel<true>, dim3((uint32_t)blocks), dim3(kRopeBlock),
-                           lds, stream, p);
+    // Whole lines per instruction when each half (R bf16 = 2R bytes / 2) and
+    // every row start are multiples of 128 bytes.
+    bool lines = p.R % 64 == 0;
+    for (int v = 0; v < p.n_views; ++v) {
+        const RopeView &V = p.v[v];
+        lines = lines && V.xs_h % 64 == 0 && V.os_h % 64 == 0 && V.xs_s % 64 == 0 &&
+                V.os_s % 64 == 0 && ((uintptr_t)V.x & 127) == 0 && ((uintptr_t)V.out & 127) == 0;
+    }
+    const dim3 grid((uint32_t)blocks), block(kRopeBlock);
+    if (p.tok_per_wg == 1 && lines)
+        hipLaunchKernelGGL((rope_rotate_half_kernel<true, true>), grid, block, lds, stream, p);
+    else if (p.tok_per_wg == 1)
+        hipLaunchKernelGGL((rope_rotate_half_kernel<true, false>), grid, block, lds, stream, p);
+    else if (lines)
+        hipLaunchKernelGGL((rope_rotate_half_kernel<false, true>), grid, block, lds, stream, p);
     else
-        hipLaunchKernelGGL(rope_rotate_half_kernel<false>, dim3((uint32_t)blocks),
-                           dim3(kRopeBlock), lds, stream, p);
+        hipLaunchKernelGGL((rope_rotate_half_kernel<false, false>), grid, block, lds, stream, p);
     return hipGetLastError();
 }
 

@@ -139,6 +139,22 @@ def test_cossin_adversarial(orc):
     assert_ulp_bar(host(s), os_, "sin strided")
 
 
+def test_cossin_mixed_paired_rows(orc):
+    """Rows whose two halves repeat (cat(f, f)) next to rows whose halves
+    differ, in the same waves: both branches of the paired table kernel."""
+    say("cos/sin mixed paired / unpaired rows")
+    S, B, R = 97, 3, 32
+    fr = W.freqs_unpaired(S, B, R, 4040)
+    rep = (np.arange(S) % 3) == 0
+    fr[rep, :, :, R // 2:] = fr[rep, :, :, :R // 2]
+    fr[5, 1, 0, R // 2] = -0.0
+    fr[5, 1, 0, 0] = 0.0
+    gc, gs = gpu_cossin(fr)
+    oc, os_ = orc.rope_cossin(fr)
+    assert_ulp_bar(gc, oc, "cos mixed rows")
+    assert_ulp_bar(gs, os_, "sin mixed rows")
+
+
 def test_cossin_empty_and_guards(orc):
     say("cos/sin empty shapes and guard bands")
     f = torch.zeros((0, 2, 1, 16), device="cuda")
