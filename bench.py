@@ -304,25 +304,52 @@ def _per_dispatch(rows, counter, symbol):
     return sorted(vals.values())
 
 
+def _short_kernel(name):
+    for v in KERNEL_SYMBOL.values():
+        if v in name:
+            return v
+    return "build_gelu_table_kernel" if "gelu_table" in name else None
+
+
 def trace_summary(d, out, command):
-    """Short markdown table of a rocprofv3 --kernel-trace --stats run."""
-    paths = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
-    rows = []
-    for path in paths:
+    """Short markdown summary of a rocprofv3 --kernel-trace run: the --stats
+    table if present, and the median dispatch duration of each run of
+    consecutive dispatches of one kernel and grid (one workload of a sweep)."""
+    lines = ["# rocprofv3 kernel trace", "", f"Command: `{command}`", ""]
+    stats = []
+    for path in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
         with open(path) as f:
-            rows.extend(csv.DictReader(f))
-    lines = ["# rocprofv3 kernel trace, dit_layer workload", "",
-             f"Command: `{command}`", "",
-             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
-    for row in rows:
-        name = row["Name"]
-        short = next((v for v in KERNEL_SYMBOL.values() if v in name), None)
-        if short is None and "gelu_table" not in name:
-            continue
-        short = short or "build_gelu_table_kernel"
-        lines.append(f"| {short} | {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | "
-                     f"{float(row['MinNs']) / 1e3:.2f} | {float(row['MaxNs']) / 1e3:.2f} |")
-    lines.append("")
+            stats.extend(csv.DictReader(f))
+    if stats:
+        lines += ["| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+        for row in stats:
+            short = _short_kernel(row["Name"])
+            if short:
+                lines.append(f"| {short} | {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | "
+                             f"{float(row['MinNs']) / 1e3:.2f} | {float(row['MaxNs']) / 1e3:.2f} |")
+        lines.append("")
+    trace = []
+    for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            trace.extend(csv.DictReader(f))
+    trace = [r for r in trace if _short_kernel(r["Kernel_Name"])]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    runs = []
+    for r in trace:
+        key = (_short_kernel(r["Kernel_Name"]), r["Grid_Size_X"], r["Workgroup_Size_X"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if runs and runs[-1][0] == key:
+            runs[-1][1].append(dur)
+        else:
+            runs.append((key, [dur]))
+    if runs:
+        lines += ["Dispatch durations, consecutive runs in launch order:", "",
+                  "| kernel | grid threads | workgroup | dispatches | median us | min us |",
+                  "|---|---|---|---|---|---|"]
+        for (k, g, w), ds in runs:
+            ds.sort()
+            lines.append(f"| {k} | {g} | {w} | {len(ds)} | {ds[len(ds) // 2]:.2f} | {ds[0]:.2f} |")
+        lines.append("")
     text = "\n".join(lines)
     if out:
         with open(out, "w") as f:
