@@ -32,6 +32,9 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
 #ifndef RGG_GEGLU_BLOCK
 #define RGG_GEGLU_BLOCK 512      // GEGLU workgroup size
 #endif
+#ifndef RGG_GEGLU_VEC
+#define RGG_GEGLU_VEC 1          // 16-byte vectors per lane (loads all issued first)
+#endif
 #ifndef RGG_GEGLU_WG_PER_CU
 #define RGG_GEGLU_WG_PER_CU 0    // 0: one vector per lane, one pass per workgroup;
 #endif                           // n: n resident workgroups per CU, grid-stride loop
@@ -40,6 +43,9 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
 #endif
 #ifndef RGG_ROPE_BLOCK
 #define RGG_ROPE_BLOCK 256       // RoPE workgroup size
+#endif
+#ifndef RGG_ROPE_UNROLL
+#define RGG_ROPE_UNROLL 1        // RoPE items per lane with their loads issued together
 #endif
 #ifndef RGG_ROPE_LDS
 #define RGG_ROPE_LDS 1           // 1: stage cos/sin rows in LDS; 0: read them per item
@@ -325,6 +331,8 @@ __device__ __forceinline__ void load_bf16x8_as_f32(const uint16_t *src, float *d
     dst[4] = bf_lo(w.z); dst[5] = bf_hi(w.z); dst[6] = bf_lo(w.w); dst[7] = bf_hi(w.w);
 }
 
+constexpr int kRopeUnroll = RGG_ROPE_UNROLL;
+
 template <bool OneToken, bool Nt>
 __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams p)
 {
@@ -347,67 +355,68 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
     if (OneToken)
         rope_token_base(p, V, (uint32_t)t0, xb1, ob1);
 
-    // First item: loads in flight before the staging barrier.
-    int i = tid;
-    RopeItem it{};
-    v4u x1{}, x2{};
-    if (i < items) {
-        it = rope_locate<OneToken>(p, V, t0, i, slots, div_slots, xb1, ob1);
-        x1 = load16<Nt>(V.x + it.xo);
-        if (it.rot)
-            x2 = load16<Nt>(V.x + it.xo + half);
-    }
-
-#if RGG_ROPE_LDS
-    // Stage this workgroup's cos/sin rows (consecutive table rows) as fp32.
-    {
-        const v4u *gc = reinterpret_cast<const v4u *>(p.cos + t0 * R);
-        const v4u *gs = reinterpret_cast<const v4u *>(p.sin + t0 * R);
-        const int nvec = ntok * (R / 8);
-        for (int k = tid; k < nvec; k += kRopeBlock) {
-            v4u c = gc[k], sn = gs[k];
-            float4 *dc = reinterpret_cast<float4 *>(lcos + k * 8);
-            float4 *ds = reinterpret_cast<float4 *>(lsin + k * 8);
-            dc[0] = make_float4(bf_lo(c.x), bf_hi(c.x), bf_lo(c.y), bf_hi(c.y));
-            dc[1] = make_float4(bf_lo(c.z), bf_hi(c.z), bf_lo(c.w), bf_hi(c.w));
-            ds[0] = make_float4(bf_lo(sn.x), bf_hi(sn.x), bf_lo(sn.y), bf_hi(sn.y));
-            ds[1] = make_float4(bf_lo(sn.z), bf_hi(sn.z), bf_lo(sn.w), bf_hi(sn.w));
+    constexpr int U = kRopeUnroll;
+    for (int base = 0; base < items; base += kRopeBlock * U) {
+        // Locate and load U items per lane before anything waits.  Lanes past
+        // the end re-read the last item and tail items read their vector
+        // twice, so no load sits under a branch.
+        RopeItem it[U];
+        v4u x1[U], x2[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int ic = min(base + u * kRopeBlock + tid, items - 1);
+            it[u] = rope_locate<OneToken>(p, V, t0, ic, slots, div_slots, xb1, ob1);
+            x1[u] = load16<Nt>(V.x + it[u].xo);
+            x2[u] = load16<Nt>(V.x + it[u].xo + (it[u].rot ? half : 0));
         }
-    }
-    __syncthreads();
-#endif
-
-    while (i < items) {
-        if (it.rot) {
-            float c1[8], s1[8], c2[8], s2[8];
 #if RGG_ROPE_LDS
-            load_f32x8(lcos + it.co, c1);
-            load_f32x8(lsin + it.co, s1);
-            load_f32x8(lcos + it.co + half, c2);
-            load_f32x8(lsin + it.co + half, s2);
+        if (base == 0) {
+            // Stage this workgroup's cos/sin rows (consecutive table rows) as
+            // fp32 while the x loads are in flight.
+            const v4u *gc = reinterpret_cast<const v4u *>(p.cos + t0 * R);
+            const v4u *gs = reinterpret_cast<const v4u *>(p.sin + t0 * R);
+            const int nvec = ntok * (R / 8);
+            for (int k = tid; k < nvec; k += kRopeBlock) {
+                v4u c = gc[k], sn = gs[k];
+                float4 *dc = reinterpret_cast<float4 *>(lcos + k * 8);
+                float4 *ds = reinterpret_cast<float4 *>(lsin + k * 8);
+                dc[0] = make_float4(bf_lo(c.x), bf_hi(c.x), bf_lo(c.y), bf_hi(c.y));
+                dc[1] = make_float4(bf_lo(c.z), bf_hi(c.z), bf_lo(c.w), bf_hi(c.w));
+                ds[0] = make_float4(bf_lo(sn.x), bf_hi(sn.x), bf_lo(sn.y), bf_hi(sn.y));
+                ds[1] = make_float4(bf_lo(sn.z), bf_hi(sn.z), bf_lo(sn.w), bf_hi(sn.w));
+            }
+            __syncthreads();
+        }
+#endif
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (base + u * kRopeBlock + tid >= items)
+                continue;
+            if (it[u].rot) {
+                float c1[8], s1[8], c2[8], s2[8];
+#if RGG_ROPE_LDS
+                load_f32x8(lcos + it[u].co, c1);
+                load_f32x8(lsin + it[u].co, s1);
+                load_f32x8(lcos + it[u].co + half, c2);
+                load_f32x8(lsin + it[u].co + half, s2);
 #else
-            const int64_t cg = t0 * R + it.co;
-            load_bf16x8_as_f32(p.cos + cg, c1);
-            load_bf16x8_as_f32(p.sin + cg, s1);
-            load_bf16x8_as_f32(p.cos + cg + half, c2);
-            load_bf16x8_as_f32(p.sin + cg + half, s2);
+                const int64_t cg = t0 * R + it[u].co;
+                load_bf16x8_as_f32(p.cos + cg, c1);
+                load_bf16x8_as_f32(p.sin + cg, s1);
+                load_bf16x8_as_f32(p.cos + cg + half, c2);
+                load_bf16x8_as_f32(p.sin + cg + half, s2);
 #endif
-            uint32_t a[4], b[4];
-            rope_word(x1.x, x2.x, c1 + 0, s1 + 0, c2 + 0, s2 + 0, a[0], b[0]);
-            rope_word(x1.y, x2.y, c1 + 2, s1 + 2, c2 + 2, s2 + 2, a[1], b[1]);
-            rope_word(x1.z, x2.z, c1 + 4, s1 + 4, c2 + 4, s2 + 4, a[2], b[2]);
-            rope_word(x1.w, x2.w, c1 + 6, s1 + 6, c2 + 6, s2 + 6, a[3], b[3]);
-            store16<Nt>(V.out + it.oo, v4u{a[0], a[1], a[2], a[3]});
-            store16<Nt>(V.out + it.oo + half, v4u{b[0], b[1], b[2], b[3]});
-        } else {
-            store16<Nt>(V.out + it.oo, x1);
-        }
-        i += kRopeBlock;
-        if (i < items) {
-            it = rope_locate<OneToken>(p, V, t0, i, slots, div_slots, xb1, ob1);
-            x1 = load16<Nt>(V.x + it.xo);
-            if (it.rot)
-                x2 = load16<Nt>(V.x + it.xo + half);
+                const v4u a1 = x1[u], a2 = x2[u];
+                uint32_t a[4], b[4];
+                rope_word(a1.x, a2.x, c1 + 0, s1 + 0, c2 + 0, s2 + 0, a[0], b[0]);
+                rope_word(a1.y, a2.y, c1 + 2, s1 + 2, c2 + 2, s2 + 2, a[1], b[1]);
+                rope_word(a1.z, a2.z, c1 + 4, s1 + 4, c2 + 4, s2 + 4, a[2], b[2]);
+                rope_word(a1.w, a2.w, c1 + 6, s1 + 6, c2 + 6, s2 + 6, a[3], b[3]);
+                store16<Nt>(V.out + it[u].oo, v4u{a[0], a[1], a[2], a[3]});
+                store16<Nt>(V.out + it[u].oo + half, v4u{b[0], b[1], b[2], b[3]});
+            } else {
+                store16<Nt>(V.out + it[u].oo, x1[u]);
+            }
         }
     }
 }
@@ -517,37 +526,48 @@ __device__ __forceinline__ v4u geglu_vec(v4u g, v4u u, const uint16_t *lut)
 }
 
 constexpr int kGegluBlock = RGG_GEGLU_BLOCK;
+constexpr int kGegluVec = RGG_GEGLU_VEC;
 
 __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p)
 {
     __shared__ __align__(16) uint16_t lut[kLutEntries];
     const uint32_t nvec_row = p.div_vecs.d;
-    const uint32_t step = gridDim.x * kGegluBlock;
-    uint32_t idx = blockIdx.x * kGegluBlock + threadIdx.x;
+    const uint32_t chunk = kGegluBlock * kGegluVec;
+    const uint32_t step = gridDim.x * chunk;
+    uint32_t base = blockIdx.x * chunk;
 
-    v4u g{}, u{};
-    int64_t oo = 0;
-    auto fetch = [&](uint32_t j) {
-        uint32_t row = fdiv(j, p.div_vecs);
-        uint32_t col = (j - row * nvec_row) * 8;
-        const uint16_t *src = p.in + (int64_t)row * p.in_stride + col;
-        g = stream_load(src);
-        u = stream_load(src + p.hidden);
-        oo = (int64_t)row * p.out_stride + col;
+    v4u g[kGegluVec], u[kGegluVec];
+    int64_t oo[kGegluVec];
+    auto fetch = [&](uint32_t b0) {
+#pragma unroll
+        for (int k = 0; k < kGegluVec; ++k) {
+            // lanes past the end re-read the last vector (no load under a branch)
+            uint32_t j = min(b0 + k * kGegluBlock + threadIdx.x, p.vec_total - 1);
+            uint32_t row = fdiv(j, p.div_vecs);
+            uint32_t col = (j - row * nvec_row) * 8;
+            const uint16_t *src = p.in + (int64_t)row * p.in_stride + col;
+            g[k] = stream_load(src);
+            u[k] = stream_load(src + p.hidden);
+            oo[k] = (int64_t)row * p.out_stride + col;
+        }
     };
-    if (idx < p.vec_total)
-        fetch(idx);
+    if (base < p.vec_total)
+        fetch(base);
 
     for (uint32_t k = threadIdx.x; k < kLutEntries / 8; k += kGegluBlock)
         reinterpret_cast<v4u *>(lut)[k] = reinterpret_cast<const v4u *>(g_gelu_lut)[k];
     __syncthreads();
 
-    while (idx < p.vec_total) {
-        v4u o = geglu_vec(g, u, lut);
-        stream_store(p.out + oo, o);
-        idx += step;
-        if (idx < p.vec_total)
-            fetch(idx);
+    while (base < p.vec_total) {
+#pragma unroll
+        for (int k = 0; k < kGegluVec; ++k) {
+            v4u o = geglu_vec(g[k], u[k], lut);
+            if (base + k * kGegluBlock + threadIdx.x < p.vec_total)
+                stream_store(p.out + oo[k], o);
+        }
+        base += step;
+        if (base < p.vec_total)
+            fetch(base);
     }
 }
 
@@ -631,9 +651,9 @@ int rope_tokens_per_workgroup(int H, int D, int R)
 
 int geglu_grid(uint32_t vec_total, int cu_count)
 {
-    // One vector per lane; with RGG_GEGLU_WG_PER_CU > 0 the grid is capped at
-    // that many workgroups per compute unit and each loops (grid stride).
-    const uint32_t chunk = kGegluBlock;
+    // kGegluVec vectors per lane; with RGG_GEGLU_WG_PER_CU > 0 the grid is
+    // capped at that many workgroups per compute unit and each loops.
+    const uint32_t chunk = kGegluBlock * kGegluVec;
     uint32_t chunks = (vec_total + chunk - 1) / chunk;
     if (chunks == 0)
         chunks = 1;

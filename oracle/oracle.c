@@ -35,6 +35,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_API __attribute__((visibility("default")))
@@ -179,32 +180,44 @@ static void rope_row(const double *x, const double *c, const double *s,
         out[j] = x[j];
 }
 
+/* One row in the eager bf16 policy; `work` holds 4*D doubles. */
+static void rope_row_bf16(const uint16_t *x_row, const uint16_t *cos_row,
+                          const uint16_t *sin_row, int64_t D, int64_t R, double *work,
+                          uint16_t *out_row)
+{
+    double *x = work, *c = work + D, *s = work + 2 * D, *o = work + 3 * D;
+    for (int64_t j = 0; j < D; ++j)
+        x[j] = oracle_bf16_to_double(x_row[j]);
+    for (int64_t j = 0; j < R; ++j) {
+        c[j] = oracle_bf16_to_double(cos_row[j]);
+        s[j] = oracle_bf16_to_double(sin_row[j]);
+    }
+    rope_row(x, c, s, D, R, to_bf16_value, o);
+    for (int64_t j = 0; j < R; ++j)
+        out_row[j] = oracle_double_to_bf16(o[j], 0);
+    for (int64_t j = R; j < D; ++j)
+        out_row[j] = x_row[j]; /* tail: the bits themselves */
+}
+
+#define ORACLE_MAX_D 65536
+
 /*
  * Rows form: n independent rows of width D; row i is rotated with cos/sin
  * row i (cos_rows/sin_rows are (n, R)).  All arrays contiguous bf16 bits.
  */
-#define ORACLE_MAX_D 4096
-
 ORACLE_API int oracle_rope_rows(const uint16_t *x_rows, const uint16_t *cos_rows,
                                 const uint16_t *sin_rows, int64_t n, int64_t D, int64_t R,
                                 uint16_t *out_rows)
 {
-    double x[ORACLE_MAX_D], c[ORACLE_MAX_D], s[ORACLE_MAX_D], o[ORACLE_MAX_D];
-    if (D < 0 || D > ORACLE_MAX_D || R < 0 || R > D || R % 2 != 0)
+    if (D < 1 || D > ORACLE_MAX_D || R < 0 || R > D || R % 2 != 0)
         return -1;
-    for (int64_t i = 0; i < n; ++i) {
-        for (int64_t j = 0; j < D; ++j)
-            x[j] = oracle_bf16_to_double(x_rows[i * D + j]);
-        for (int64_t j = 0; j < R; ++j) {
-            c[j] = oracle_bf16_to_double(cos_rows[i * R + j]);
-            s[j] = oracle_bf16_to_double(sin_rows[i * R + j]);
-        }
-        rope_row(x, c, s, D, R, to_bf16_value, o);
-        for (int64_t j = 0; j < R; ++j)
-            out_rows[i * D + j] = oracle_double_to_bf16(o[j], 0);
-        for (int64_t j = R; j < D; ++j)
-            out_rows[i * D + j] = x_rows[i * D + j]; /* tail: the bits themselves */
-    }
+    double *work = malloc(4 * (size_t)D * sizeof(double));
+    if (!work)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        rope_row_bf16(x_rows + i * D, cos_rows + i * R, sin_rows + i * R, D, R, work,
+                      out_rows + i * D);
+    free(work);
     return 0;
 }
 
@@ -216,16 +229,20 @@ ORACLE_API int oracle_rope_rotate_half(const uint16_t *x, int64_t B, int64_t S, 
                                        int64_t D, int64_t R, const uint16_t *cos_tab,
                                        const uint16_t *sin_tab, uint16_t *out)
 {
-    if (D < 0 || D > ORACLE_MAX_D || R < 0 || R > D || R % 2 != 0)
+    if (D < 1 || D > ORACLE_MAX_D || R < 0 || R > D || R % 2 != 0)
+        return -1;
+    double *work = malloc(4 * (size_t)D * sizeof(double));
+    if (!work)
         return -1;
     for (int64_t b = 0; b < B; ++b)
         for (int64_t s = 0; s < S; ++s)
             for (int64_t hh = 0; hh < H; ++hh) {
                 int64_t row = b * S + s;
                 int64_t at = ((b * S + s) * H + hh) * D;
-                oracle_rope_rows(x + at, cos_tab + row * R, sin_tab + row * R, 1, D, R,
-                                 out + at);
+                rope_row_bf16(x + at, cos_tab + row * R, sin_tab + row * R, D, R, work,
+                              out + at);
             }
+    free(work);
     return 0;
 }
 

@@ -9,6 +9,7 @@ and the Python binding's own argument checks.  No call here reaches a launch.
 import ctypes
 import os
 import re
+import sys
 import subprocess
 
 import pytest
@@ -176,3 +177,9 @@ def test_binding_rejects_host_tensors():
 def test_binding_error_carries_status(lib):
     err = rgg.RggError("f", ALIAS, lib.rgg_status_string(ALIAS).decode())
     assert err.status == ALIAS and "overlaps" in str(err)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr

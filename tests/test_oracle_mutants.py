@@ -26,8 +26,8 @@ MUTANTS = {
         "double partner = (j < h) ? -x[j + h] : x[j - h];",
         "double partner = (j < h) ? -x[j] : x[j];"),
     "tail_dropped": (
-        "out_rows[i * D + j] = x_rows[i * D + j]; /* tail: the bits themselves */",
-        "out_rows[i * D + j] = 0;"),
+        "out_row[j] = x_row[j]; /* tail: the bits themselves */",
+        "out_row[j] = 0;"),
     "table_row_s_major": (
         "            int64_t row = b * S + s;\n            for (int64_t j = 0; j < R; ++j) {",
         "            int64_t row = s * B + b;\n            for (int64_t j = 0; j < R; ++j) {"),

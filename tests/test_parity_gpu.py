@@ -469,3 +469,118 @@ def test_geglu_full_size(orc, wid):
     bad = int((diff & ~nan).sum())
     say(f"geglu w{wid} whole tensor vs up*T[gate]: {bad} of {out.numel()} differ")
     assert bad == 0
+
+
+# ---------------------------------------------------------------------------
+# layouts, limits, graphs
+# ---------------------------------------------------------------------------
+
+def test_rope_into_attention_layout(orc):
+    """Outputs written straight into a (B, H, S, D) buffer (the layout an
+    attention kernel reads) through output strides, q and k in one launch."""
+    B, S, H, D, R = 2, 40, 6, 64, 64
+    say("rope into (B,H,S,D) outputs")
+    q = W.normal_bf16((B, S, H, D), 8401)
+    k = W.normal_bf16((B, S, H, D), 8402)
+    cos, sin = orc.rope_cossin(W.freqs_unpaired(S, B, R, 8403))
+    oq = torch.empty((B, H, S, D), dtype=torch.bfloat16, device="cuda")
+    ok = torch.empty((B, H, S, D), dtype=torch.bfloat16, device="cuda")
+    rgg.rope_rotate_half_bf16([dev(q), dev(k)], dev(cos), dev(sin),
+                              out=[oq.permute(0, 2, 1, 3), ok.permute(0, 2, 1, 3)])
+    assert_bitexact(host(oq).transpose(0, 2, 1, 3), oracle_rope(orc, q, cos, sin), "q -> BHSD")
+    assert_bitexact(host(ok).transpose(0, 2, 1, 3), oracle_rope(orc, k, cos, sin), "k -> BHSD")
+
+
+@pytest.mark.parametrize("shape", [(1, 3, 2, 2048, 1024), (1, 5, 1, 8192, 4096),
+                                   (2, 7, 3, 512, 512), (1, 2, 4, 1024, 16)],
+                         ids=["D2048R1024", "D8192R4096", "D512R512", "D1024R16"])
+def test_rope_wide_heads(orc, shape):
+    """Head widths up to the 8192-column limit, with and without tails."""
+    B, S, H, D, R = shape
+    say(f"rope wide heads {shape}")
+    x = W.special_bf16((B, S, H, D), 8500 + D)
+    cos, sin = orc.rope_cossin(W.freqs_unpaired(S, B, R, 8501 + D))
+    out = rgg.rope_rotate_half_bf16(dev(x), dev(cos), dev(sin))
+    assert_bitexact(host(out), oracle_rope(orc, x, cos, sin), f"wide {shape}")
+
+
+def test_geglu_wide_rows(orc):
+    say("geglu wide rows")
+    inp = W.special_bf16((3, 2 * 65536), 8601)
+    out = host(rgg.gelu_and_mul_bf16(dev(inp)))
+    want = orc.gelu_and_mul(inp)
+    nan = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
+    assert_ulp_bar(out[~nan], want[~nan], "geglu 3 x 65536")
+
+
+def test_graph_capture_replays(orc):
+    """All three entry points captured in one HIP graph and replayed several
+    times, with eager work and synchronisation between replays; every replay
+    matches the eager result."""
+    say("graph capture of the whole path")
+    rgg.prepare_device(0)
+    B, S, H, D, R = 1, 64, 4, 64, 64
+    fr = torch.from_numpy(W.freqs_1d(S, B, R)).cuda()
+    x = dev(W.normal_bf16((B, S, H, D), 8701))
+    inp = dev(W.normal_bf16((96, 2 * 128), 8702, 2.0))
+    cos = torch.empty((B * S, R), dtype=torch.bfloat16, device="cuda")
+    sin = torch.empty_like(cos)
+    xo = torch.empty_like(x)
+    go = torch.empty((96, 128), dtype=torch.bfloat16, device="cuda")
+
+    def path():
+        rgg.rope_cossin_precompute(fr, cos, sin)
+        rgg.rope_rotate_half_bf16(x, cos, sin, out=xo)
+        rgg.gelu_and_mul_bf16(inp, go)
+
+    path()
+    want = [host(t).copy() for t in (cos, sin, xo, go)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        path()
+    for rep in range(4):
+        for t in (cos, sin, xo, go):
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [host(t) for t in (cos, sin, xo, go)]
+        for g, w, name in zip(got, want, ("cos", "sin", "rope", "geglu")):
+            assert np.array_equal(g, w), f"replay {rep}: {name} differs from eager"
+        _ = (x.float() * 2).sum().item()  # eager work between replays
+
+
+def test_first_gelu_call_while_capturing_is_refused():
+    """In a fresh process, a first GEGLU call made under graph capture returns
+    RGG_ERR_CAPTURING instead of building its table; rgg_prepare_device then
+    makes capture work."""
+    import subprocess
+    import sys
+    code = r"""
+import sys
+sys.path.insert(0, %r)
+import torch
+import bf16_rope_geglu_amd as rgg
+inp = torch.zeros((8, 16), dtype=torch.bfloat16, device="cuda")
+out = torch.empty((8, 8), dtype=torch.bfloat16, device="cuda")
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+status = None
+with torch.cuda.graph(g):
+    try:
+        rgg.gelu_and_mul_bf16(inp, out)
+    except rgg.RggError as e:
+        status = e.status
+print("status", status, flush=True)
+rgg.prepare_device(0)
+g2 = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g2):
+    rgg.gelu_and_mul_bf16(inp, out)
+g2.replay()
+torch.cuda.synchronize()
+print("ok", flush=True)
+""" % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=240)
+    say(r.stdout.strip())
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "status 7" in r.stdout and "ok" in r.stdout
