@@ -47,6 +47,12 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
 #ifndef RGG_ROPE_UNROLL
 #define RGG_ROPE_UNROLL 1        // RoPE items per lane with their loads issued together
 #endif
+#ifndef RGG_ROPE_ORDER
+#define RGG_ROPE_ORDER 0         // workgroup order: 0 view fastest, 1 view slowest, 2 XCD-contiguous
+#endif
+#ifndef RGG_ROPE_WAVE_STAGE
+#define RGG_ROPE_WAVE_STAGE 1    // one-token RoPE: each wave stages its own cos/sin copy (no barrier)
+#endif
 #ifndef RGG_ROPE_LDS
 #define RGG_ROPE_LDS 1           // 1: stage cos/sin rows in LDS; 0: read them per item
 #endif
@@ -341,8 +347,28 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
     float *lcos = reinterpret_cast<float *>(smem);  // [tpw][R]
     float *lsin = lcos + tpw * R;                   // [tpw][R]
 
-    const uint32_t wg_tok = fdiv(blockIdx.x, p.div_views);
-    const int v = (int)(blockIdx.x - wg_tok * (uint32_t)p.n_views);
+    uint32_t wg = blockIdx.x;
+#if RGG_ROPE_ORDER == 2
+    {
+        // Workgroups are dealt to the 8 XCDs round robin; renumber so that
+        // XCD k walks one contiguous eighth of the work.
+        const uint32_t n = gridDim.x, per = n / 8;
+        if (wg < per * 8)
+            wg = (wg % 8) * per + wg / 8;
+    }
+#endif
+    uint32_t wg_tok;
+    int v;
+#if RGG_ROPE_ORDER == 1
+    {
+        const uint32_t nchunks = (uint32_t)((p.tokens + tpw - 1) / tpw);
+        v = (int)(wg / nchunks);
+        wg_tok = wg - (uint32_t)v * nchunks;
+    }
+#else
+    wg_tok = fdiv(wg, p.div_views);
+    v = (int)(wg - wg_tok * (uint32_t)p.n_views);
+#endif
     const int64_t t0 = (int64_t)wg_tok * tpw;
     const int ntok = (int)min((int64_t)tpw, p.tokens - t0);
     const RopeView V = p.v[v];
@@ -369,8 +395,31 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
             x1[u] = load16<Nt>(V.x + it[u].xo);
             x2[u] = load16<Nt>(V.x + it[u].xo + (it[u].rot ? half : 0));
         }
+#if RGG_ROPE_LDS && RGG_ROPE_WAVE_STAGE
+        if (OneToken && base == 0) {
+            // One token: every wave stages its own fp32 copy of the row in
+            // its own LDS slot, so no wave waits for another.  LDS operations
+            // of one wave complete in order; the wave barrier keeps the
+            // compiler from moving the reads above the writes.
+            const int wave = tid >> 6, lane = tid & 63;
+            float *wc = lcos + wave * 2 * R, *ws = wc + R;
+            const v4u *gc = reinterpret_cast<const v4u *>(p.cos + t0 * R);
+            const v4u *gs = reinterpret_cast<const v4u *>(p.sin + t0 * R);
+            for (int k = lane; k < R / 4; k += 64) {
+                const bool is_sin = k >= R / 8;
+                const int kk = is_sin ? k - R / 8 : k;
+                v4u c = is_sin ? gs[kk] : gc[kk];
+                float4 *d = reinterpret_cast<float4 *>((is_sin ? ws : wc) + kk * 8);
+                d[0] = make_float4(bf_lo(c.x), bf_hi(c.x), bf_lo(c.y), bf_hi(c.y));
+                d[1] = make_float4(bf_lo(c.z), bf_hi(c.z), bf_lo(c.w), bf_hi(c.w));
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+#endif
 #if RGG_ROPE_LDS
-        if (base == 0) {
+        if ((!OneToken || !RGG_ROPE_WAVE_STAGE) && base == 0) {
             // Stage this workgroup's cos/sin rows (consecutive table rows) as
             // fp32 while the x loads are in flight.
             const v4u *gc = reinterpret_cast<const v4u *>(p.cos + t0 * R);
@@ -395,10 +444,15 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
             if (it[u].rot) {
                 float c1[8], s1[8], c2[8], s2[8];
 #if RGG_ROPE_LDS
-                load_f32x8(lcos + it[u].co, c1);
-                load_f32x8(lsin + it[u].co, s1);
-                load_f32x8(lcos + it[u].co + half, c2);
-                load_f32x8(lsin + it[u].co + half, s2);
+                const float *rc = lcos, *rs = lsin;
+                if (OneToken && RGG_ROPE_WAVE_STAGE) {
+                    rc = lcos + (tid >> 6) * 2 * R;
+                    rs = rc + R;
+                }
+                load_f32x8(rc + it[u].co, c1);
+                load_f32x8(rs + it[u].co, s1);
+                load_f32x8(rc + it[u].co + half, c2);
+                load_f32x8(rs + it[u].co + half, s2);
 #else
                 const int64_t cg = t0 * R + it[u].co;
                 load_bf16x8_as_f32(p.cos + cg, c1);
@@ -601,6 +655,8 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
     p.div_views = make_fastdiv((uint32_t)p.n_views);
     int64_t blocks = (p.tokens + p.tok_per_wg - 1) / p.tok_per_wg * p.n_views;
     size_t lds = RGG_ROPE_LDS ? (size_t)p.tok_per_wg * p.R * 2 * sizeof(float) : 0;
+    if (RGG_ROPE_LDS && RGG_ROPE_WAVE_STAGE && p.tok_per_wg == 1)
+        lds = (size_t)(kRopeBlock / 64) * p.R * 2 * sizeof(float);
     // Whole lines per instruction when each half (R bf16 = 2R bytes / 2) and
     // every row start are multiples of 128 bytes.
     bool lines = p.R % 64 == 0;
