@@ -2,6 +2,9 @@
 
     python -m bf16_rope_geglu_amd.build
 
+build_capi_client() also compiles tests/host/capi_client.c, a plain C program
+that drives the library through include/rgg.h with no Python in the way.
+
 Flags: -ffp-contract=off keeps every multiply and add a separate IEEE op
 (the bf16 rounding sits between them); packed-fp32 instructions are disabled;
 symbols other than the C ABI are hidden.
@@ -41,5 +44,27 @@ def build(out=LIBRARY, extra=()):
     return out
 
 
+CLIENT_SOURCE = os.path.join(ROOT, "tests", "host", "capi_client.c")
+CLIENT = os.path.join(ROOT, "tests", "host", "_bin", "capi_client")
+ROCM_LIB = "/opt/rocm/lib"
+
+
+def build_capi_client(out=CLIENT, library=LIBRARY):
+    """Compile the C client against `library` with gcc (C11, -Werror)."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    libdir = os.path.dirname(library)
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror",
+           "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}", "-I/opt/rocm/include",
+           CLIENT_SOURCE, "-o", out + ".tmp",
+           f"-L{libdir}", "-lrgg", f"-L{ROCM_LIB}", "-lamdhip64",
+           f"-Wl,-rpath,{libdir}", f"-Wl,-rpath,{ROCM_LIB}"]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError("gcc failed:\n" + proc.stdout + proc.stderr)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build())
+    print(build_capi_client())

@@ -183,3 +183,11 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_c_client_compiles_as_c11(tmp_path):
+    """include/rgg.h is usable from plain C: the client builds with gcc -Werror."""
+    import bf16_rope_geglu_amd.build as libbuild
+
+    exe = libbuild.build_capi_client(out=os.path.join(tmp_path, "capi_client"))
+    assert os.path.exists(exe)

@@ -584,3 +584,43 @@ print("ok", flush=True)
     say(r.stdout.strip())
     assert r.returncode == 0, r.stderr[-2000:]
     assert "status 7" in r.stdout and "ok" in r.stdout
+
+
+# ---------------------------------------------------------------------------
+# The C ABI from plain C: tests/host/capi_client.c, no Python in between
+# ---------------------------------------------------------------------------
+
+CLIENT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "host", "_bin", "capi_client")
+
+
+def test_plain_c_client(orc, tmp_path):
+    import subprocess
+
+    assert os.path.exists(CLIENT), "tests/host/_bin/capi_client is not built"
+    S, B, H, D, R, rows, hidden = 300, 2, 3, 64, 48, 77, 136
+    say(f"C client: rope ({B},{S},{H},{D}) R={R}, geglu ({rows},{hidden})")
+    freqs = W.freqs_unpaired(S, B, R, 71)
+    x = W.normal_bf16((B, S, H, D), 72)
+    inp = np.concatenate([W.normal_bf16((rows, hidden), 73, 2.0),
+                          W.normal_bf16((rows, hidden), 74)], axis=1)
+    src, dst = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(src, "wb") as f:
+        f.write(np.array([S, B, H, D, R, rows, hidden], np.int64).tobytes())
+        f.write(np.ascontiguousarray(freqs, np.float32).tobytes())
+        f.write(np.ascontiguousarray(x, np.uint16).tobytes())
+        f.write(np.ascontiguousarray(inp, np.uint16).tobytes())
+    proc = subprocess.run([CLIENT, str(src), str(dst)], capture_output=True, text=True,
+                          timeout=60)
+    say(proc.stdout.strip(), proc.stderr.strip())
+    assert proc.returncode == 0, f"capi_client exit status {proc.returncode}"
+    got = np.fromfile(dst, np.uint16)
+    n_t, n_x = B * S * R, x.size
+    assert got.size == 2 * n_t + n_x + rows * hidden
+    cos, sin = got[:n_t].reshape(B * S, R), got[n_t:2 * n_t].reshape(B * S, R)
+    rope = got[2 * n_t:2 * n_t + n_x].reshape(x.shape)
+    geglu = got[2 * n_t + n_x:].reshape(rows, hidden)
+    oc, os_ = orc.rope_cossin(freqs)
+    assert_ulp_bar(cos, oc, "C client cos")
+    assert_ulp_bar(sin, os_, "C client sin")
+    assert_bitexact(rope, oracle_rope(orc, x, cos, sin), "C client rope")
+    assert_ulp_bar(geglu, orc.gelu_and_mul(inp), "C client geglu")
