@@ -53,6 +53,9 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
 #ifndef RGG_ROPE_WAVE_STAGE
 #define RGG_ROPE_WAVE_STAGE 1    // one-token RoPE: each wave stages its own cos/sin copy (no barrier)
 #endif
+#ifndef RGG_ROPE_LANE
+#define RGG_ROPE_LANE 1          // one-token launches whose half-rotation splits 128-byte lines:
+#endif                           // one contiguous output vector per lane
 #ifndef RGG_ROPE_LDS
 #define RGG_ROPE_LDS 1           // 1: stage cos/sin rows in LDS; 0: read them per item
 #endif
@@ -475,6 +478,89 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
     }
 }
 
+#if RGG_ROPE_LANE
+// One output vector per lane: lane i of the workgroup writes 16-byte vector i
+// of the token's head rows, so every load and store instruction of a wave
+// covers whole contiguous lines for any R.  The lane also loads its
+// rotate-half partner vector (R/2 columns away, in the same lines, served
+// from cache) and applies
+//   first half:  out = rne(rne(x*c) + rne(-x_partner*s)),
+//   second half: out = rne(rne(x*c) + rne(x_partner*s)),
+// negating a bf16 by its sign bit, which is exact.
+__device__ __forceinline__ uint32_t rope_word1(uint32_t a, uint32_t b, const float *c,
+                                              const float *s)
+{
+    uint32_t p0 = rne_pack(bf_lo(a) * c[0], bf_lo(b) * s[0]);
+    uint32_t p1 = rne_pack(bf_hi(a) * c[1], bf_hi(b) * s[1]);
+    return rne_pack(bf_lo(p0) + bf_hi(p0), bf_lo(p1) + bf_hi(p1));
+}
+
+template <bool Nt, int U>
+__global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeParams p)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int R = p.R, nv = p.D / 8, rv = R / 8, hv = R / 16;
+    const uint32_t wg = blockIdx.x;
+    const uint32_t t = fdiv(wg, p.div_views);
+    const int v = (int)(wg - t * (uint32_t)p.n_views);
+    const RopeView V = p.v[v];
+    int64_t xb, ob;
+    rope_token_base(p, V, t, xb, ob);
+    const int items = p.H * nv;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    float *wc = reinterpret_cast<float *>(smem) + wave * 2 * R, *ws = wc + R;
+
+    for (int base = 0; base < items; base += kRopeBlock * U) {
+        int64_t oo[U];
+        int j[U];
+        v4u a[U], b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int ic = min(base + u * kRopeBlock + tid, items - 1);
+            const uint32_t h = fdiv((uint32_t)ic, p.div_vecs);
+            j[u] = ic - (int)h * nv;
+            const int64_t xo = xb + (int64_t)h * V.xs_h + j[u] * 8;
+            oo[u] = ob + (int64_t)h * V.os_h + j[u] * 8;
+            const int pj = j[u] < hv ? hv : (j[u] < rv ? -hv : 0);
+            a[u] = load16<Nt>(V.x + xo);
+            b[u] = load16<false>(V.x + xo + pj * 8);
+        }
+        if (base == 0) {
+            const v4u *gc = reinterpret_cast<const v4u *>(p.cos + (int64_t)t * R);
+            const v4u *gs = reinterpret_cast<const v4u *>(p.sin + (int64_t)t * R);
+            for (int k = lane; k < R / 4; k += 64) {
+                const bool is_sin = k >= R / 8;
+                const int kk = is_sin ? k - R / 8 : k;
+                v4u c = is_sin ? gs[kk] : gc[kk];
+                float4 *d = reinterpret_cast<float4 *>((is_sin ? ws : wc) + kk * 8);
+                d[0] = make_float4(bf_lo(c.x), bf_hi(c.x), bf_lo(c.y), bf_hi(c.y));
+                d[1] = make_float4(bf_lo(c.z), bf_hi(c.z), bf_lo(c.w), bf_hi(c.w));
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (base + u * kRopeBlock + tid >= items)
+                continue;
+            if (j[u] < rv) {
+                float c[8], s[8];
+                load_f32x8(wc + j[u] * 8, c);
+                load_f32x8(ws + j[u] * 8, s);
+                const uint32_t flip = j[u] < hv ? 0x80008000u : 0u;
+                const v4u x = a[u], y = b[u] ^ flip;
+                store16<Nt>(V.out + oo[u],
+                            v4u{rope_word1(x.x, y.x, c + 0, s + 0), rope_word1(x.y, y.y, c + 2, s + 2),
+                                rope_word1(x.z, y.z, c + 4, s + 4), rope_word1(x.w, y.w, c + 6, s + 6)});
+            } else {
+                store16<Nt>(V.out + oo[u], a[u]);
+            }
+        }
+    }
+}
+#endif
+
 // ---------------------------------------------------------------------------
 // (a4, a5) GEGLU with activation rounding             [ERNIE-fuse §3]
 //
@@ -666,6 +752,29 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
                 V.os_s % 64 == 0 && ((uintptr_t)V.x & 127) == 0 && ((uintptr_t)V.out & 127) == 0;
     }
     const dim3 grid((uint32_t)blocks), block(kRopeBlock);
+#if RGG_ROPE_LANE
+    // When R/2 is not a whole number of 128-byte lines the two-vector items
+    // split lines between store instructions; one contiguous vector per lane
+    // keeps every line whole.
+    const int all_tails = (1 << p.n_views) - 1;
+    if (p.tok_per_wg == 1 && p.tail_mask == all_tails && p.R > 0 && !lines) {
+        bool whole = p.D % 64 == 0;
+        for (int v = 0; v < p.n_views; ++v) {
+            const RopeView &V = p.v[v];
+            whole = whole && V.xs_h % 64 == 0 && V.os_h % 64 == 0 && V.xs_s % 64 == 0 &&
+                    V.os_s % 64 == 0 && ((uintptr_t)V.x & 127) == 0 && ((uintptr_t)V.out & 127) == 0;
+        }
+        if (whole) {
+            p.div_vecs = make_fastdiv((uint32_t)(p.D / 8));
+            lds = (size_t)(kRopeBlock / 64) * p.R * 2 * sizeof(float);
+            if ((int64_t)p.H * (p.D / 8) >= 2 * kRopeBlock)
+                hipLaunchKernelGGL((rope_rotate_half_lane_kernel<true, 2>), grid, block, lds, stream, p);
+            else
+                hipLaunchKernelGGL((rope_rotate_half_lane_kernel<true, 1>), grid, block, lds, stream, p);
+            return hipGetLastError();
+        }
+    }
+#endif
     if (p.tok_per_wg == 1 && lines)
         hipLaunchKernelGGL((rope_rotate_half_kernel<true, true>), grid, block, lds, stream, p);
     else if (p.tok_per_wg == 1)

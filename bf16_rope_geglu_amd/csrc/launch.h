@@ -51,6 +51,7 @@ struct RopeParams {
     FastDiv div_heads;     // divisor H
     FastDiv div_slots;     // divisor R/16: item -> (token-local, head, slot), no tail
     FastDiv div_slots_tail;  // divisor slots_tail
+    FastDiv div_vecs;      // divisor D/8: vector index -> (head, vector of the head row)
 };
 
 struct CosSinParams {

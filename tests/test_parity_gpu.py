@@ -219,6 +219,7 @@ ADVERSARIAL = [  # B, S, H, D, R, views, data, tables
     (1, 5, 1, 16, 0, 1, "normal", "none"),
     (1, 1, 1, 16, 16, 1, "special", "special"),
     (5, 3, 33, 24, 16, 2, "normal", "unpaired"),
+    (1, 23, 24, 128, 96, 2, "special", "unpaired"),
 ]
 
 
@@ -492,8 +493,10 @@ def test_rope_into_attention_layout(orc):
 
 
 @pytest.mark.parametrize("shape", [(1, 3, 2, 2048, 1024), (1, 5, 1, 8192, 4096),
-                                   (2, 7, 3, 512, 512), (1, 2, 4, 1024, 16)],
-                         ids=["D2048R1024", "D8192R4096", "D512R512", "D1024R16"])
+                                   (2, 7, 3, 512, 512), (1, 2, 4, 1024, 16),
+                                   (2, 9, 20, 128, 112), (1, 4, 3, 1024, 1008)],
+                         ids=["D2048R1024", "D8192R4096", "D512R512", "D1024R16",
+                              "H20D128R112", "D1024R1008"])
 def test_rope_wide_heads(orc, shape):
     """Head widths up to the 8192-column limit, with and without tails."""
     B, S, H, D, R = shape
