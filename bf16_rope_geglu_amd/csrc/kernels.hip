@@ -56,6 +56,9 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
 #ifndef RGG_ROPE_LANE
 #define RGG_ROPE_LANE 1          // one-token launches whose half-rotation splits 128-byte lines:
 #endif                           // one contiguous output vector per lane
+#ifndef RGG_ROPE_LANE_U2_MIN
+#define RGG_ROPE_LANE_U2_MIN 512 // one-vector lanes: two vectors per lane from this many per token
+#endif
 #ifndef RGG_ROPE_LDS
 #define RGG_ROPE_LDS 1           // 1: stage cos/sin rows in LDS; 0: read them per item
 #endif
@@ -398,8 +401,8 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
             x1[u] = load16<Nt>(V.x + it[u].xo);
             x2[u] = load16<Nt>(V.x + it[u].xo + (it[u].rot ? half : 0));
         }
-#if RGG_ROPE_LDS && RGG_ROPE_WAVE_STAGE
-        if (OneToken && base == 0) {
+#if RGG_ROPE_LDS
+        if (OneToken && p.wave_stage && base == 0) {
             // One token: every wave stages its own fp32 copy of the row in
             // its own LDS slot, so no wave waits for another.  LDS operations
             // of one wave complete in order; the wave barrier keeps the
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
         }
 #endif
 #if RGG_ROPE_LDS
-        if ((!OneToken || !RGG_ROPE_WAVE_STAGE) && base == 0) {
+        if ((!OneToken || !p.wave_stage) && base == 0) {
             // Stage this workgroup's cos/sin rows (consecutive table rows) as
             // fp32 while the x loads are in flight.
             const v4u *gc = reinterpret_cast<const v4u *>(p.cos + t0 * R);
@@ -448,7 +451,7 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
                 float c1[8], s1[8], c2[8], s2[8];
 #if RGG_ROPE_LDS
                 const float *rc = lcos, *rs = lsin;
-                if (OneToken && RGG_ROPE_WAVE_STAGE) {
+                if (OneToken && p.wave_stage) {
                     rc = lcos + (tid >> 6) * 2 * R;
                     rs = rc + R;
                 }
@@ -741,8 +744,12 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
     p.div_views = make_fastdiv((uint32_t)p.n_views);
     int64_t blocks = (p.tokens + p.tok_per_wg - 1) / p.tok_per_wg * p.n_views;
     size_t lds = RGG_ROPE_LDS ? (size_t)p.tok_per_wg * p.R * 2 * sizeof(float) : 0;
-    if (RGG_ROPE_LDS && RGG_ROPE_WAVE_STAGE && p.tok_per_wg == 1)
-        lds = (size_t)(kRopeBlock / 64) * p.R * 2 * sizeof(float);
+    // One-token workgroups give each wave its own staged row unless the
+    // copies would crowd LDS (wide rotations); then the workgroup shares one.
+    const size_t wave_lds = (size_t)(kRopeBlock / 64) * p.R * 2 * sizeof(float);
+    p.wave_stage = RGG_ROPE_LDS && RGG_ROPE_WAVE_STAGE && p.tok_per_wg == 1 && wave_lds <= 65536;
+    if (p.wave_stage)
+        lds = wave_lds;
     // Whole lines per instruction when each half (R bf16 = 2R bytes / 2) and
     // every row start are multiples of 128 bytes.
     bool lines = p.R % 64 == 0;
@@ -757,7 +764,7 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
     // split lines between store instructions; one contiguous vector per lane
     // keeps every line whole.
     const int all_tails = (1 << p.n_views) - 1;
-    if (p.tok_per_wg == 1 && p.tail_mask == all_tails && p.R > 0 && !lines) {
+    if (p.wave_stage && p.tail_mask == all_tails && p.R > 0 && !lines) {
         bool whole = p.D % 64 == 0;
         for (int v = 0; v < p.n_views; ++v) {
             const RopeView &V = p.v[v];
@@ -766,8 +773,7 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
         }
         if (whole) {
             p.div_vecs = make_fastdiv((uint32_t)(p.D / 8));
-            lds = (size_t)(kRopeBlock / 64) * p.R * 2 * sizeof(float);
-            if ((int64_t)p.H * (p.D / 8) >= 2 * kRopeBlock)
+            if ((int64_t)p.H * (p.D / 8) >= RGG_ROPE_LANE_U2_MIN)
                 hipLaunchKernelGGL((rope_rotate_half_lane_kernel<true, 2>), grid, block, lds, stream, p);
             else
                 hipLaunchKernelGGL((rope_rotate_half_lane_kernel<true, 1>), grid, block, lds, stream, p);

@@ -494,9 +494,10 @@ def test_rope_into_attention_layout(orc):
 
 @pytest.mark.parametrize("shape", [(1, 3, 2, 2048, 1024), (1, 5, 1, 8192, 4096),
                                    (2, 7, 3, 512, 512), (1, 2, 4, 1024, 16),
-                                   (2, 9, 20, 128, 112), (1, 4, 3, 1024, 1008)],
+                                   (2, 9, 20, 128, 112), (1, 4, 3, 1024, 1008),
+                                   (1, 3, 1, 8192, 8192)],
                          ids=["D2048R1024", "D8192R4096", "D512R512", "D1024R16",
-                              "H20D128R112", "D1024R1008"])
+                              "H20D128R112", "D1024R1008", "D8192R8192"])
 def test_rope_wide_heads(orc, shape):
     """Head widths up to the 8192-column limit, with and without tails."""
     B, S, H, D, R = shape
