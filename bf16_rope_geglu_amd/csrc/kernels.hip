@@ -47,9 +47,6 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
 #ifndef RGG_ROPE_UNROLL
 #define RGG_ROPE_UNROLL 1        // RoPE items per lane with their loads issued together
 #endif
-#ifndef RGG_ROPE_ORDER
-#define RGG_ROPE_ORDER 0         // workgroup order: 0 view fastest, 1 view slowest, 2 XCD-contiguous
-#endif
 #ifndef RGG_ROPE_WAVE_STAGE
 #define RGG_ROPE_WAVE_STAGE 1    // one-token RoPE: each wave stages its own cos/sin copy (no barrier)
 #endif
@@ -335,6 +332,7 @@ __device__ __forceinline__ RopeItem rope_locate(const RopeParams &p, const RopeV
 }
 
 constexpr int kRopeBlock = RGG_ROPE_BLOCK;
+constexpr int64_t kMaxRopeWorkgroups = (int64_t)1 << 20;  // per launch (2^28 work-items)
 
 __device__ __forceinline__ void load_bf16x8_as_f32(const uint16_t *src, float *dst)
 {
@@ -353,28 +351,9 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
     float *lcos = reinterpret_cast<float *>(smem);  // [tpw][R]
     float *lsin = lcos + tpw * R;                   // [tpw][R]
 
-    uint32_t wg = blockIdx.x;
-#if RGG_ROPE_ORDER == 2
-    {
-        // Workgroups are dealt to the 8 XCDs round robin; renumber so that
-        // XCD k walks one contiguous eighth of the work.
-        const uint32_t n = gridDim.x, per = n / 8;
-        if (wg < per * 8)
-            wg = (wg % 8) * per + wg / 8;
-    }
-#endif
-    uint32_t wg_tok;
-    int v;
-#if RGG_ROPE_ORDER == 1
-    {
-        const uint32_t nchunks = (uint32_t)((p.tokens + tpw - 1) / tpw);
-        v = (int)(wg / nchunks);
-        wg_tok = wg - (uint32_t)v * nchunks;
-    }
-#else
-    wg_tok = fdiv(wg, p.div_views);
-    v = (int)(wg - wg_tok * (uint32_t)p.n_views);
-#endif
+    const uint32_t wg = blockIdx.x;
+    const uint32_t wg_tok = p.chunk0 + fdiv(wg, p.div_views);
+    const int v = (int)(wg - (wg_tok - p.chunk0) * (uint32_t)p.n_views);
     const int64_t t0 = (int64_t)wg_tok * tpw;
     const int ntok = (int)min((int64_t)tpw, p.tokens - t0);
     const RopeView V = p.v[v];
@@ -504,8 +483,8 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
     extern __shared__ __align__(16) unsigned char smem[];
     const int R = p.R, nv = p.D / 8, rv = R / 8, hv = R / 16;
     const uint32_t wg = blockIdx.x;
-    const uint32_t t = fdiv(wg, p.div_views);
-    const int v = (int)(wg - t * (uint32_t)p.n_views);
+    const uint32_t t = p.chunk0 + fdiv(wg, p.div_views);
+    const int v = (int)(wg - (t - p.chunk0) * (uint32_t)p.n_views);
     const RopeView V = p.v[v];
     int64_t xb, ob;
     rope_token_base(p, V, t, xb, ob);
@@ -742,7 +721,6 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
     RopeParams p = params;
     p.tok_per_wg = rope_tokens_per_workgroup(p.H, p.D, p.R);
     p.div_views = make_fastdiv((uint32_t)p.n_views);
-    int64_t blocks = (p.tokens + p.tok_per_wg - 1) / p.tok_per_wg * p.n_views;
     size_t lds = RGG_ROPE_LDS ? (size_t)p.tok_per_wg * p.R * 2 * sizeof(float) : 0;
     // One-token workgroups give each wave its own staged row unless the
     // copies would crowd LDS (wide rotations); then the workgroup shares one.
@@ -758,7 +736,15 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
         lines = lines && V.xs_h % 64 == 0 && V.os_h % 64 == 0 && V.xs_s % 64 == 0 &&
                 V.os_s % 64 == 0 && ((uintptr_t)V.x & 127) == 0 && ((uintptr_t)V.out & 127) == 0;
     }
-    const dim3 grid((uint32_t)blocks), block(kRopeBlock);
+    void (*kernel)(RopeParams);
+    if (p.tok_per_wg == 1 && lines)
+        kernel = rope_rotate_half_kernel<true, true>;
+    else if (p.tok_per_wg == 1)
+        kernel = rope_rotate_half_kernel<true, false>;
+    else if (lines)
+        kernel = rope_rotate_half_kernel<false, true>;
+    else
+        kernel = rope_rotate_half_kernel<false, false>;
 #if RGG_ROPE_LANE
     // When R/2 is not a whole number of 128-byte lines the two-vector items
     // split lines between store instructions; one contiguous vector per lane
@@ -774,22 +760,29 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
         if (whole) {
             p.div_vecs = make_fastdiv((uint32_t)(p.D / 8));
             if ((int64_t)p.H * (p.D / 8) >= RGG_ROPE_LANE_U2_MIN)
-                hipLaunchKernelGGL((rope_rotate_half_lane_kernel<true, 2>), grid, block, lds, stream, p);
+                kernel = rope_rotate_half_lane_kernel<true, 2>;
             else
-                hipLaunchKernelGGL((rope_rotate_half_lane_kernel<true, 1>), grid, block, lds, stream, p);
-            return hipGetLastError();
+                kernel = rope_rotate_half_lane_kernel<true, 1>;
         }
     }
 #endif
-    if (p.tok_per_wg == 1 && lines)
-        hipLaunchKernelGGL((rope_rotate_half_kernel<true, true>), grid, block, lds, stream, p);
-    else if (p.tok_per_wg == 1)
-        hipLaunchKernelGGL((rope_rotate_half_kernel<true, false>), grid, block, lds, stream, p);
-    else if (lines)
-        hipLaunchKernelGGL((rope_rotate_half_kernel<false, true>), grid, block, lds, stream, p);
-    else
-        hipLaunchKernelGGL((rope_rotate_half_kernel<false, false>), grid, block, lds, stream, p);
-    return hipGetLastError();
+    // A dispatch's grid is counted in 32-bit work-items, so very long token
+    // ranges go out as several launches of at most kMaxRopeWorkgroups.
+    const int64_t chunks = (p.tokens + p.tok_per_wg - 1) / p.tok_per_wg;
+    const int64_t per_launch = kMaxRopeWorkgroups / p.n_views;
+    for (int64_t c0 = 0; c0 < chunks; c0 += per_launch) {
+        p.chunk0 = (uint32_t)c0;
+        const int64_t n = chunks - c0 < per_launch ? chunks - c0 : per_launch;
+        void *args[] = {&p};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel),
+                                       dim3((uint32_t)(n * p.n_views)), dim3(kRopeBlock), args,
+                                       lds, stream);
+        if (e == hipSuccess)
+            e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_gelu_and_mul(const GegluParams &p, int grid, hipStream_t stream)

@@ -47,6 +47,7 @@ struct RopeParams {
     int32_t tail_mask;     // bit v set: copy the tail of view v
     int32_t slots_tail;    // R/16 + (D - R)/8 work slots per head when the tail is copied
     int32_t wave_stage;    // one-token workgroups: each wave stages its own cos/sin row
+    uint32_t chunk0;       // first token chunk of this launch (long ranges take several)
     FastDiv div_s;         // token -> (b, s)
     FastDiv div_views;     // workgroup -> (token chunk, view)
     FastDiv div_heads;     // divisor H

@@ -508,6 +508,31 @@ def test_rope_wide_heads(orc, shape):
     assert_bitexact(host(out), oracle_rope(orc, x, cos, sin), f"wide {shape}")
 
 
+@pytest.mark.parametrize("R", [16, 64], ids=["lane_path", "slot_path"])
+def test_rope_launch_split_over_many_workgroups(orc, R):
+    """4 views x 262147 one-token workgroups is more than one launch takes
+    (2^20 workgroups), so the call is split; tokens on both sides of the split
+    and at the ends are checked.  Inputs are stride-0 views of one row per
+    view, so only the outputs take memory (4 x 1.1 GB)."""
+    B, S, H, D, nv = 1, 262147, 1, 2112, 4
+    say(f"rope split launch: S={S} H={H} D={D} R={R} views={nv}")
+    rows = [W.special_bf16((1, 1, H, D), 8600 + R + v) for v in range(nv)]
+    cos = W.normal_bf16((B * S, R), 8610 + R)
+    sin = W.normal_bf16((B * S, R), 8620 + R)
+    xs = [dev(r).expand(B, S, H, D) for r in rows]
+    outs = [torch.empty((B, S, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(nv)]
+    rgg.rope_rotate_half_bf16(xs, dev(cos), dev(sin), out=outs)
+    split = (1 << 20) // nv
+    rng = np.random.Generator(np.random.PCG64(8630))
+    tokens = sorted({0, 1, split - 1, split, split + 1, S - 1} |
+                    set(rng.integers(0, S, 16).tolist()))
+    for v in range(nv):
+        got = np.stack([host(outs[v][0, t]) for t in tokens])
+        want = np.stack([orc.rope_rotate_half(rows[v], cos[t:t + 1], sin[t:t + 1])[0, 0]
+                         for t in tokens])
+        assert_bitexact(got, want, f"view {v}, tokens {tokens[:6]}...")
+
+
 def test_geglu_wide_rows(orc):
     say("geglu wide rows")
     inp = W.special_bf16((3, 2 * 65536), 8601)
