@@ -23,6 +23,12 @@ changed since the counters were taken.
 turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs (DIR/fetch, DIR/write)
 into that summary; --calibration-copy adds a plain device copy of known size
 to each step so the same runs calibrate the counters.
+
+    python bench.py --sweep
+prints a markdown table of every kernel on every workload with cold caches
+(replayed from one HIP graph), each beside the streaming reference
+(bf16_rope_geglu_amd/lib/libstreamref.so) moving the same bytes with the
+same read:write ratio: the practical ceiling for that traffic.
 """
 import argparse
 import csv
@@ -152,6 +158,23 @@ def run_gpu(args):
 # per-kernel sweep over every workload, cold caches
 # ---------------------------------------------------------------------------
 
+def stream_ref_library():
+    """ctypes handle of bf16_rope_geglu_amd/lib/libstreamref.so (built by
+    __graft_entry__.build()), the streaming reference timed in the sweep."""
+    import ctypes
+
+    import torch  # noqa: F401  (loads the HIP runtime the library links)
+
+    path = os.path.join(ROOT, "bf16_rope_geglu_amd", "lib", "libstreamref.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    lib.rgg_stream_ref.restype = ctypes.c_int
+    lib.rgg_stream_ref.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
 def run_sweep(reps=40, touch=2 << 30):
     """Per-launch time of each kernel on each workload.  Enough input and
     output sets are allocated that consecutive launches touch `touch` bytes
@@ -168,6 +191,7 @@ def run_sweep(reps=40, touch=2 << 30):
     torch.cuda.set_device(dev)
     rgg.prepare_device(0)
     rows_out = []
+    ref = stream_ref_library()
 
     def timed(fns, nbytes):
         for f in fns:
@@ -188,6 +212,26 @@ def run_sweep(reps=40, touch=2 << 30):
         us = a.elapsed_time(b) * 1e3 / reps
         del graph
         return us, nbytes / (us * 1e-6) / 1e9
+
+    def stream_us(nbytes, reads):
+        """Per-launch time of the streaming reference moving nbytes with
+        `reads` reads per write (same cold-cache rotation), the faster of
+        256- and 512-thread workgroups."""
+        wbytes = nbytes // (1 + reads)
+        nsets = max(2, -(-touch // nbytes))
+        sets = [[torch.empty(wbytes, dtype=torch.uint8, device=dev) for _ in range(reads + 1)]
+                for _ in range(nsets)]
+
+        def launch(st, block):
+            b = st[1].data_ptr() if reads == 2 else None
+            status = ref.rgg_stream_ref(st[0].data_ptr(), b, st[-1].data_ptr(), wbytes // 16,
+                                        block, torch.cuda.current_stream(dev).cuda_stream)
+            if status:
+                raise RuntimeError(f"rgg_stream_ref returned {status}")
+        best = min(timed([(lambda st=st, blk=blk: launch(st, blk)) for st in sets], nbytes)[0]
+                   for blk in (256, 512))
+        del sets
+        return best
 
     for wid, wl in sorted(W.WORKLOADS.items()):
         if wid == 0:
@@ -216,7 +260,8 @@ def run_sweep(reps=40, touch=2 << 30):
             for name, fns in (("rope_cossin_precompute", pre), ("rope_rotate_half_bf16", rot)):
                 key = "precompute" if "cossin" in name else "rope"
                 us, gbps = timed(fns, algo[key])
-                rows_out.append((wl["name"], name, algo[key], nsets, us, gbps))
+                rows_out.append((wl["name"], name, algo[key], nsets, us, gbps,
+                                 stream_us(algo[key], 1)))
             del sets
         if "geglu" in wl:
             g = wl["geglu"]
@@ -228,14 +273,18 @@ def run_sweep(reps=40, touch=2 << 30):
                 sets.append((inp, out))
             fns = [(lambda st=st: rgg.gelu_and_mul_bf16(st[0], st[1])) for st in sets]
             us, gbps = timed(fns, algo["geglu"])
-            rows_out.append((wl["name"], "gelu_and_mul_bf16", algo["geglu"], nsets, us, gbps))
             del sets
+            rows_out.append((wl["name"], "gelu_and_mul_bf16", algo["geglu"], nsets, us, gbps,
+                             stream_us(algo["geglu"], 2)))
         torch.cuda.empty_cache()
 
-    print("| workload | entry point | algorithmic bytes | buffer sets | us per launch | GB/s | % of 8 TB/s |")
-    print("|---|---|---|---|---|---|---|")
-    for w, n, b, k, us, gbps in rows_out:
-        print(f"| {w} | {n} | {b} | {k} | {us:.1f} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f} |")
+    print("| workload | entry point | algorithmic bytes | buffer sets | us per launch | GB/s "
+          "| % of 8 TB/s | stream reference us (% of 8 TB/s) | kernel vs stream |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for w, n, b, k, us, gbps, sus in rows_out:
+        sfrac = 100 * b / (sus * 1e-6) / 1e9 / PEAK_HBM_GBPS
+        print(f"| {w} | {n} | {b} | {k} | {us:.1f} | {gbps:.0f} | {100 * gbps / PEAK_HBM_GBPS:.1f} "
+              f"| {sus:.1f} ({sfrac:.1f}) | {100 * sus / us:.1f}% |")
     sys.stdout.flush()
 
 
@@ -308,7 +357,10 @@ def _short_kernel(name):
     for v in KERNEL_SYMBOL.values():
         if v in name:
             return v
-    return "build_gelu_table_kernel" if "gelu_table" in name else None
+    for v in ("build_gelu_table_kernel", "stream_ref_kernel"):
+        if v in name:
+            return v
+    return None
 
 
 def trace_summary(d, out, command):

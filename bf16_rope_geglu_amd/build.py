@@ -3,7 +3,9 @@
     python -m bf16_rope_geglu_amd.build
 
 build_capi_client() also compiles tests/host/capi_client.c, a plain C program
-that drives the library through include/rgg.h with no Python in the way.
+that drives the library through include/rgg.h with no Python in the way, and
+build_stream_ref() the streaming reference kernel bench.py measures against
+(lib/libstreamref.so, not part of the C ABI).
 
 Flags: -ffp-contract=off keeps every multiply and add a separate IEEE op
 (the bf16 rounding sits between them); packed-fp32 instructions are disabled;
@@ -44,6 +46,21 @@ def build(out=LIBRARY, extra=()):
     return out
 
 
+STREAM_REF_SOURCE = os.path.join(CSRC, "stream_ref.hip")
+STREAM_REF = os.path.join(LIBDIR, "libstreamref.so")
+
+
+def build_stream_ref(out=STREAM_REF):
+    """Compile the streaming reference that bench.py times beside each kernel."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    cmd = [HIPCC, *FLAGS, STREAM_REF_SOURCE, "-o", out + ".tmp"]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + proc.stdout + proc.stderr)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 CLIENT_SOURCE = os.path.join(ROOT, "tests", "host", "capi_client.c")
 CLIENT = os.path.join(ROOT, "tests", "host", "_bin", "capi_client")
 ROCM_LIB = "/opt/rocm/lib"
@@ -68,3 +85,4 @@ def build_capi_client(out=CLIENT, library=LIBRARY):
 if __name__ == "__main__":
     print(build())
     print(build_capi_client())
+    print(build_stream_ref())

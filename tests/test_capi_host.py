@@ -191,3 +191,15 @@ def test_c_client_compiles_as_c11(tmp_path):
 
     exe = libbuild.build_capi_client(out=os.path.join(tmp_path, "capi_client"))
     assert os.path.exists(exe)
+
+
+def test_stream_reference_loads_and_checks_arguments():
+    """The streaming reference bench.py times beside the kernels: exported,
+    and bad arguments are refused before anything reaches a device."""
+    import bench
+
+    ref = bench.stream_ref_library()
+    assert ref.rgg_stream_ref(A, None, A + 4096, 0, 256, None) == 2
+    assert ref.rgg_stream_ref(A, None, A + 4096, 16, 96, None) == 2
+    assert ref.rgg_stream_ref(A + 8, None, A + 4096, 16, 256, None) == 2
+    assert ref.rgg_stream_ref(None, None, A + 4096, 16, 256, None) == 2
