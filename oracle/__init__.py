@@ -39,6 +39,10 @@ class Oracle:
         lib.oracle_double_to_bf16.restype = ctypes.c_uint16
         lib.oracle_rope_cossin.argtypes = [_f32p, _i64, _i64, _i64, _i64, _i64, _u16p, _u16p]
         lib.oracle_rope_cossin.restype = None
+        lib.oracle_rope_angles_grid.restype = None
+        lib.oracle_rope_angles_grid.argtypes = [_i64, _i64, _i64, _i64,
+                                                ctypes.POINTER(ctypes.c_int32), ctypes.c_double,
+                                                ctypes.POINTER(ctypes.c_int32), _f32p]
         lib.oracle_rope_rows.argtypes = [_u16p, _u16p, _u16p, _i64, _i64, _i64, _u16p]
         lib.oracle_rope_rows.restype = ctypes.c_int
         lib.oracle_rope_rotate_half.argtypes = [_u16p, _i64, _i64, _i64, _i64, _i64,
@@ -89,6 +93,28 @@ class Oracle:
         base = freqs.ctypes.data_as(_f32p)
         self.lib.oracle_rope_cossin(base, S, B, R, ss, sb, _ptr(cos, _u16p), _ptr(sin, _u16p))
         return cos, sin
+
+    def rope_angles_grid(self, B, grid, dims, theta, t_offset=None):
+        """fp32 angles (S, B, 1, R) of a (T, Hg, Wg) token grid with axis
+        column counts `dims` (3 even ints); t_offset: B ints or None."""
+        T, Hg, Wg = (int(v) for v in grid)
+        d = np.ascontiguousarray(dims, np.int32)
+        assert d.shape == (3,) and (d % 2 == 0).all()
+        S, R = T * Hg * Wg, int(d.sum())
+        out = np.empty((S, B, 1, R), np.float32)
+        off = None
+        if t_offset is not None:
+            off = np.ascontiguousarray(t_offset, np.int32)
+            assert off.shape == (B,)
+        self.lib.oracle_rope_angles_grid(
+            B, T, Hg, Wg, _ptr(d, ctypes.POINTER(ctypes.c_int32)), float(theta),
+            None if off is None else _ptr(off, ctypes.POINTER(ctypes.c_int32)),
+            _ptr(out, _f32p))
+        return out
+
+    def rope_cossin_grid(self, B, grid, dims, theta, t_offset=None):
+        """The (B*S, R) cos/sin tables of the grid's angles."""
+        return self.rope_cossin(self.rope_angles_grid(B, grid, dims, theta, t_offset))
 
     # -- (a2, a3) rotate-half ------------------------------------------------
     def rope_rotate_half(self, x, cos, sin):

@@ -31,7 +31,9 @@
  * bf16 chunk/neg/cat/mul/add chain run by PyTorch on the CPU, hand-derived
  * worked vectors, the zero-angle identity, exact-arithmetic rotation
  * invariants, mpmath at 256-bit precision (cos, sin, and every one of the
- * 65536 bf16 GELU inputs) and textbook values of the normal CDF.
+ * 65536 bf16 GELU inputs), textbook values of the normal CDF, and, for the
+ * grid angles, a numpy form of the same reading plus exact products in
+ * mpmath.
  */
 #include <math.h>
 #include <stdint.h>
@@ -146,6 +148,49 @@ ORACLE_API void oracle_rope_cossin(const float *freqs, int64_t S, int64_t B, int
                 double f = (double)freqs[s * stride_s + b * stride_b + j];
                 cos_out[row * R + j] = oracle_double_to_bf16(cos(f), 0);
                 sin_out[row * R + j] = oracle_double_to_bf16(sin(f), 0);
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * (f2) rotary angles of a 3-axis token grid       [ERNIE-fuse §1, the angles
+ *                                                  the table hoist is fed]
+ *
+ * The page hoists the tables from angles that the model's 3-axis positional
+ * embedding (EmbedND3) produces, and does not define that step.  Reading
+ * used here, the plain one for a rotate-half model over a (T, Hg, Wg) token
+ * grid:
+ *   - token s sits at (t, h, w) with s = (t*Hg + h)*Wg + w; batch row b
+ *     shifts t by t_offset[b] (no shift when t_offset is NULL);
+ *   - axis k, owning d_k rotary columns, contributes d_k/2 half-angles
+ *     pos_k * theta^(-2i/d_k), i = 0 .. d_k/2 - 1;
+ *   - the three axes' half-angles, axis 0 first, form f (R/2 values, with
+ *     R = d_0 + d_1 + d_2), and the angle row is cat(f, f), so that column j
+ *     and column j + R/2 turn by the same angle;
+ *   - each half-angle is formed in double and rounded once to float.
+ * The result is the fp32 angle tensor (S, B, 1, R), S = T*Hg*Wg, contiguous,
+ * that oracle_rope_cossin turns into the tables.
+ * ------------------------------------------------------------------------- */
+ORACLE_API void oracle_rope_angles_grid(int64_t B, int64_t T, int64_t Hg, int64_t Wg,
+                                        const int32_t *dims, double theta,
+                                        const int32_t *t_offset, float *freqs)
+{
+    const int64_t S = T * Hg * Wg;
+    const int64_t R = (int64_t)dims[0] + dims[1] + dims[2], half = R / 2;
+    for (int64_t s = 0; s < S; ++s) {
+        const int64_t t = s / (Hg * Wg), h = (s / Wg) % Hg, w = s % Wg;
+        for (int64_t b = 0; b < B; ++b) {
+            const double pos[3] = {(double)(t + (t_offset ? t_offset[b] : 0)), (double)h,
+                                   (double)w};
+            float *row = freqs + (s * B + b) * R;
+            int64_t j = 0;
+            for (int k = 0; k < 3; ++k) {
+                for (int32_t i = 0; i < dims[k] / 2; ++i, ++j) {
+                    const double omega = pow(theta, -2.0 * i / dims[k]);
+                    row[j] = (float)(pos[k] * omega);
+                    row[j + half] = row[j];
+                }
             }
         }
     }

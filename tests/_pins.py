@@ -258,6 +258,57 @@ def check_cossin_row_order(o):
 
 
 # ---------------------------------------------------------------------------
+# (f2) rotary angles of a 3-axis token grid
+# ---------------------------------------------------------------------------
+
+GRID_CASES = [  # B, grid, dims, theta, t_offset
+    (1, (1, 64, 64), (32, 48, 48), 1e4, None),
+    (2, (2, 8, 16), (24, 36, 36), 1e4, [0, 7]),
+    (3, (3, 5, 7), (2, 4, 10), 256.0, [4, 0, 2]),
+]
+
+
+def check_angles_grid_vs_numpy_recipe(o):
+    """The angles equal, bit for bit, the numpy form of the same reading
+    (workloads.freqs_3axis: meshgrid positions, axis-wise outer products in
+    float64, concatenation, cat(f, f), one cast to float32)."""
+    for B, grid, dims, theta, off in GRID_CASES:
+        got = o.rope_angles_grid(B, grid, dims, theta, off)
+        want = workloads.freqs_3axis(grid, dims, B, theta=theta, batch_offsets=off)
+        assert got.shape == want.shape
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (grid, dims)
+
+
+def check_angles_grid_closed_forms(o):
+    """Closed forms of the reading: the first half-angle of each axis has
+    frequency theta^0 = 1, so it equals that axis's position exactly; the
+    second half of every row repeats the first; every angle is the exact
+    product pos * theta^(-2i/d) (mpmath, 60 digits) rounded to float32,
+    within one float32 step."""
+    B, grid, dims, theta, off = 2, (3, 4, 5), (4, 6, 8), 1e4, [0, 9]
+    a = o.rope_angles_grid(B, grid, dims, theta, off)[:, :, 0, :]
+    S, R, half = 60, 18, 9
+    s = np.arange(S)
+    t, h, w = s // 20, (s // 5) % 4, s % 5
+    for b in range(B):
+        assert np.array_equal(a[:, b, 0], (t + off[b]).astype(np.float32))
+        assert np.array_equal(a[:, b, 2], h.astype(np.float32))
+        assert np.array_equal(a[:, b, 5], w.astype(np.float32))
+    assert np.array_equal(a[..., :half], a[..., half:])
+    mpmath.mp.dps = 60
+    cols = [(0, i, 4) for i in range(2)] + [(1, i, 6) for i in range(3)] + \
+           [(2, i, 8) for i in range(4)]
+    for (k, i, d), j in zip(cols, range(half)):
+        for si in (1, 23, 59):
+            for b in range(B):
+                pos = [t[si] + off[b], h[si], w[si]][k]
+                exact = mpmath.mpf(int(pos)) * mpmath.power(mpmath.mpf(theta), mpmath.mpf(-2 * i) / d)
+                got = float(a[si, b, j])
+                ulp = float(np.spacing(np.float32(abs(got)))) if got else 2.0 ** -149
+                assert abs(mpmath.mpf(got) - exact) <= ulp, (k, i, pos)
+
+
+# ---------------------------------------------------------------------------
 # (a4, a5) GELU and the multiply
 # ---------------------------------------------------------------------------
 
@@ -353,6 +404,8 @@ ALL_CHECKS = [
     check_rope_rows_form,
     check_cossin_row_order,
     check_cossin_vs_mpmath,
+    check_angles_grid_vs_numpy_recipe,
+    check_angles_grid_closed_forms,
     check_gelu_closed_forms,
     check_gelu_exact_odd_part,
     check_gelu_and_mul_vs_eager,

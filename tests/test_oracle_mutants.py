@@ -37,6 +37,20 @@ MUTANTS = {
     "cos_in_float": (
         "double f = (double)freqs[s * stride_s + b * stride_b + j];",
         "double f = (double)(float)(freqs[s * stride_s + b * stride_b + j] * 1.0001f);"),
+    "grid_frequency_over_all_columns": (
+        "const double omega = pow(theta, -2.0 * i / dims[k]);",
+        "const double omega = pow(theta, -2.0 * i / (dims[0] + dims[1] + dims[2]));"),
+    "grid_axes_reversed": (
+        "const double pos[3] = {(double)(t + (t_offset ? t_offset[b] : 0)), (double)h,\n"
+        "                                   (double)w};",
+        "const double pos[3] = {(double)w, (double)h,\n"
+        "                                   (double)(t + (t_offset ? t_offset[b] : 0))};"),
+    "grid_second_half_not_repeated": (
+        "row[j + half] = row[j];",
+        "row[j + half] = -row[j];"),
+    "grid_offset_ignored": (
+        "(double)(t + (t_offset ? t_offset[b] : 0))",
+        "(double)t"),
     "gelu_without_sqrt2": (
         "return 0.5 * x * erfc(-x / sqrt(2.0));",
         "return 0.5 * x * erfc(-x);"),
