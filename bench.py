@@ -28,7 +28,8 @@ to each step so the same runs calibrate the counters.
 prints a markdown table of every kernel on every workload with cold caches
 (replayed from one HIP graph), each beside the streaming reference
 (bf16_rope_geglu_amd/lib/libstreamref.so) moving the same bytes with the
-same read:write ratio: the practical ceiling for that traffic.
+same read:write ratio (write-only for the tables built from grid
+positions): the practical ceiling for that traffic.
 """
 import argparse
 import csv
@@ -215,16 +216,17 @@ def run_sweep(reps=40, touch=2 << 30):
 
     def stream_us(nbytes, reads):
         """Per-launch time of the streaming reference moving nbytes with
-        `reads` reads per write (same cold-cache rotation), the faster of
-        256- and 512-thread workgroups."""
+        `reads` (0, 1 or 2) reads per write (same cold-cache rotation), the
+        faster of 256- and 512-thread workgroups."""
         wbytes = nbytes // (1 + reads)
         nsets = max(2, -(-touch // nbytes))
         sets = [[torch.empty(wbytes, dtype=torch.uint8, device=dev) for _ in range(reads + 1)]
                 for _ in range(nsets)]
 
         def launch(st, block):
+            a = st[0].data_ptr() if reads >= 1 else None
             b = st[1].data_ptr() if reads == 2 else None
-            status = ref.rgg_stream_ref(st[0].data_ptr(), b, st[-1].data_ptr(), wbytes // 16,
+            status = ref.rgg_stream_ref(a, b, st[-1].data_ptr(), wbytes // 16,
                                         block, torch.cuda.current_stream(dev).cuda_stream)
             if status:
                 raise RuntimeError(f"rgg_stream_ref returned {status}")
@@ -257,11 +259,18 @@ def run_sweep(reps=40, touch=2 << 30):
             pre = [(lambda st=st: rgg.rope_cossin_precompute(st[0], st[1], st[2])) for st in sets]
             rot = [(lambda st=st: rgg.rope_rotate_half_bf16(st[3], st[1], st[2], out=st[4]))
                    for st in sets]
-            for name, fns in (("rope_cossin_precompute", pre), ("rope_rotate_half_bf16", rot)):
-                key = "precompute" if "cossin" in name else "rope"
+            steps = [("rope_cossin_precompute", "precompute", pre, 1)]
+            fk = r["freqs"]
+            if fk["kind"] == "3axis":
+                grd = [(lambda st=st: rgg.rope_cossin_from_grid(
+                    B, fk["grid"], fk["dims"], W.THETA, cos_out=st[1], sin_out=st[2]))
+                    for st in sets]
+                steps.append(("rope_cossin_from_grid", "precompute_grid", grd, 0))
+            steps.append(("rope_rotate_half_bf16", "rope", rot, 1))
+            for name, key, fns, reads in steps:
                 us, gbps = timed(fns, algo[key])
                 rows_out.append((wl["name"], name, algo[key], nsets, us, gbps,
-                                 stream_us(algo[key], 1)))
+                                 stream_us(algo[key], reads)))
             del sets
         if "geglu" in wl:
             g = wl["geglu"]

@@ -8,6 +8,8 @@ call returns a nonzero status, these functions raise.
 Method: "[sglang] ERNIE-Image의 RoPE와 GELU-mul 융합 및 RoPE cos/sin 호이스팅을
 통한 성능 최적화" (blog.secrett2633.cloud, sglang PR 34306 analysis):
   rope_cossin_precompute  -- §1, cos/sin hoisted once per forward
+  rope_cossin_from_grid   -- §1, the same tables straight from 3-axis grid
+                             positions (a reading of the angle producer)
   rope_rotate_half_bf16   -- §2, bit-exact rotate-half RoPE, tail passthrough
   gelu_and_mul_bf16       -- §3, GEGLU with bf16 activation rounding
 The page's own Python names are kept as aliases at the bottom.
@@ -57,14 +59,16 @@ def library():
                                "`python -m bf16_rope_geglu_amd.build`")
         lib = ctypes.CDLL(LIBRARY)
         lib.rope_cossin_precompute.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _P]
+        lib.rope_cossin_from_grid.argtypes = [_I, _I, _I, _I, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_double, _P, _P, _P, _P]
         lib.rope_rotate_half_bf16.argtypes = [ctypes.POINTER(RopeView), ctypes.c_int, _I, _I, _I,
                                               _I, _I, _P, _P, _P]
         lib.gelu_and_mul_bf16.argtypes = [_P, _I, _I, _I, _P, _I, _P]
         lib.rgg_prepare_device.argtypes = [ctypes.c_int]
         lib.rgg_status_string.argtypes = [ctypes.c_int]
         lib.rgg_status_string.restype = ctypes.c_char_p
-        for f in (lib.rope_cossin_precompute, lib.rope_rotate_half_bf16, lib.gelu_and_mul_bf16,
-                  lib.rgg_prepare_device):
+        for f in (lib.rope_cossin_precompute, lib.rope_cossin_from_grid,
+                  lib.rope_rotate_half_bf16, lib.gelu_and_mul_bf16, lib.rgg_prepare_device):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -108,6 +112,38 @@ def rope_cossin_precompute(freqs, cos_out=None, sin_out=None):
         _check("rope_cossin_precompute", library().rope_cossin_precompute(
             freqs.data_ptr(), S, B, R, freqs.stride(0), freqs.stride(1),
             cos_out.data_ptr(), sin_out.data_ptr(), _stream(dev)))
+    return cos_out, sin_out
+
+
+def rope_cossin_from_grid(B, grid, dims, theta=10000.0, t_offset=None, cos_out=None,
+                          sin_out=None, device=None):
+    """cos/sin tables, each bf16 (B*S, R), of a (T, Hg, Wg) token grid's 3-axis
+    rotary angles: axis k owns dims[k] columns (half-angles pos_k *
+    theta^(-2i/dims[k])), R = sum(dims), rows b*S + s with s = (t*Hg + h)*Wg + w.
+    `t_offset`, if given, is an int32 tensor of B shifts of t on the device."""
+    T, Hg, Wg = (int(v) for v in grid)
+    d0, d1, d2 = (int(v) for v in dims)
+    S, R = T * Hg * Wg, d0 + d1 + d2
+    dev = torch.device(device) if device is not None else (
+        t_offset.device if t_offset is not None else torch.device("cuda", torch.cuda.current_device()))
+    if cos_out is None:
+        cos_out = torch.empty((B * S, R), dtype=torch.bfloat16, device=dev)
+    if sin_out is None:
+        sin_out = torch.empty((B * S, R), dtype=torch.bfloat16, device=dev)
+    for name, t in (("cos_out", cos_out), ("sin_out", sin_out)):
+        _need(t, torch.bfloat16, name)
+        if tuple(t.shape) != (B * S, R) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous ({B * S}, {R})")
+    off = None
+    if t_offset is not None:
+        _need(t_offset, torch.int32, "t_offset")
+        if tuple(t_offset.shape) != (B,) or not t_offset.is_contiguous():
+            raise ValueError(f"t_offset must be a contiguous ({B},) int32 tensor")
+        off = t_offset.data_ptr()
+    with torch.cuda.device(cos_out.device):
+        _check("rope_cossin_from_grid", library().rope_cossin_from_grid(
+            B, T, Hg, Wg, d0, d1, d2, float(theta), off, cos_out.data_ptr(), sin_out.data_ptr(),
+            _stream(cos_out.device)))
     return cos_out, sin_out
 
 

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <mutex>
 
@@ -152,6 +153,67 @@ int rope_cossin_precompute(const float *freqs, int64_t S, int64_t B, int64_t R,
     p.div_vecs = make_fastdiv((uint32_t)(R / 8));
     p.div_s = make_fastdiv((uint32_t)S);
     return rgg::launch_rope_cossin(p, stream) == hipSuccess ? RGG_OK : RGG_ERR_HIP;
+}
+
+int rope_cossin_from_grid(int64_t B, int64_t T, int64_t Hg, int64_t Wg, int32_t d0, int32_t d1,
+                          int32_t d2, double theta, const int32_t *t_offset, uint16_t *cos_out,
+                          uint16_t *sin_out, hipStream_t stream)
+{
+    if (B < 0 || T < 0 || Hg < 0 || Wg < 0 || d0 < 0 || d1 < 0 || d2 < 0 || d0 % 2 || d1 % 2 ||
+        d2 % 2 || !(theta > 0.0) || !std::isfinite(theta))
+        return RGG_ERR_SHAPE;
+    const int64_t R = (int64_t)d0 + d1 + d2;
+    if (R % 16 != 0 || R > 8192)
+        return RGG_ERR_UNSUPPORTED;
+    if (B == 0 || T == 0 || Hg == 0 || Wg == 0 || R == 0)
+        return RGG_OK;
+    if (T >= kMax32 || Hg >= kMax32 || Wg >= kMax32 || T * Hg >= kMax32 || T * Hg * Wg >= kMax32)
+        return RGG_ERR_UNSUPPORTED;
+    const int64_t S = T * Hg * Wg;
+    if (B * S >= kMax32 || B * S * (R / 16) >= kMax32)
+        return RGG_ERR_UNSUPPORTED;
+    if (!cos_out || !sin_out)
+        return RGG_ERR_NULL;
+    if (!aligned16(cos_out) || !aligned16(sin_out) || ((uintptr_t)t_offset & 3))
+        return RGG_ERR_ALIGN;
+    const int64_t tn[1] = {B * S}, tst[1] = {R};
+    Layout lc = make_layout(cos_out, 2, 1, tn, tst, R);
+    Layout ls = make_layout(sin_out, 2, 1, tn, tst, R);
+    if (may_overlap(lc, ls))
+        return RGG_ERR_ALIAS;
+    if (t_offset) {
+        const int64_t on[1] = {1}, ost[1] = {0};
+        Layout lt = make_layout(t_offset, 4, 1, on, ost, B);
+        if (may_overlap(lc, lt) || may_overlap(ls, lt))
+            return RGG_ERR_ALIAS;
+    }
+
+    rgg::CosSinGridParams p;
+    memset(&p, 0, sizeof p);
+    p.t_offset = t_offset;
+    p.cos = cos_out;
+    p.sin = sin_out;
+    p.theta = theta;
+    p.groups_total = (uint32_t)(B * S * (R / 16));
+    p.R = (int32_t)R;
+    p.h0 = d0 / 2;
+    p.h01 = (d0 + d1) / 2;
+    p.d[0] = d0;
+    p.d[1] = d1;
+    p.d[2] = d2;
+    p.div_groups = make_fastdiv((uint32_t)(R / 16));
+    p.div_s = make_fastdiv((uint32_t)S);
+    p.div_hw = make_fastdiv((uint32_t)(Hg * Wg));
+    p.div_w = make_fastdiv((uint32_t)Wg);
+    p.host_omega = R / 2 <= rgg::kGridOmegaArgs;
+    if (p.host_omega) {
+        const int32_t d[3] = {d0, d1, d2};
+        int c = 0;
+        for (int k = 0; k < 3; ++k)
+            for (int32_t i = 0; i < d[k] / 2; ++i)
+                p.omega[c++] = std::pow(theta, -2.0 * i / d[k]);
+    }
+    return rgg::launch_rope_cossin_grid(p, stream) == hipSuccess ? RGG_OK : RGG_ERR_HIP;
 }
 
 int rope_rotate_half_bf16(const rgg_rope_view *views, int n_views, int64_t B, int64_t S,

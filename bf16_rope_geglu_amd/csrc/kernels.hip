@@ -241,6 +241,67 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
 }
 
 // ---------------------------------------------------------------------------
+// (a1, from positions) cos/sin tables of a 3-axis token grid  [ERNIE-fuse §1]
+//
+// Token s of a (T, Hg, Wg) grid sits at (t, h, w), s = (t*Hg + h)*Wg + w,
+// with t shifted by the batch row's offset.  Half-column c of axis k (local
+// index i) turns by pos_k * theta^(-2i/d_k), formed in double and rounded once
+// to fp32, and the row is cat(f, f), so a lane computes 8 half-columns and
+// stores each cos/sin vector in both halves.  Each workgroup first puts the
+// frequencies theta^(-2i/d_k) of the R/2 half-columns in LDS: copied from the
+// kernel arguments (computed on the host) for up to 2*kGridOmegaArgs rotary
+// columns, evaluated on the device for wider rows.  The cos/sin of the fp32
+// angle then go through the same correctly rounded path as the precompute
+// above.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void rope_cossin_grid_kernel(CosSinGridParams p)
+{
+    extern __shared__ double lomega[];  // [R/2]
+    const int half = p.R / 2;
+    for (int c = threadIdx.x; c < half; c += kThreads) {
+        if (p.host_omega) {
+            lomega[c] = p.omega[c];
+        } else {
+            const int k = c < p.h0 ? 0 : (c < p.h01 ? 1 : 2);
+            const int i = c - (k == 0 ? 0 : (k == 1 ? p.h0 : p.h01));
+            lomega[c] = pow(p.theta, -2.0 * i / p.d[k]);
+        }
+    }
+    __syncthreads();
+    const uint32_t groups = p.div_groups.d, S = p.div_s.d, HW = p.div_hw.d, Wg = p.div_w.d;
+    for (uint32_t g = blockIdx.x * kThreads + threadIdx.x; g < p.groups_total;
+         g += gridDim.x * kThreads) {
+        const uint32_t row = fdiv(g, p.div_groups);
+        const int c0 = (int)(g - row * groups) * 8;
+        const uint32_t b = fdiv(row, p.div_s);
+        const uint32_t s = row - b * S;
+        const uint32_t t = fdiv(s, p.div_hw);
+        const uint32_t hw = s - t * HW;
+        const uint32_t h = fdiv(hw, p.div_w);
+        const uint32_t w = hw - h * Wg;
+        const double pos[3] = {(double)((int64_t)t + (p.t_offset ? p.t_offset[b] : 0)),
+                               (double)h, (double)w};
+        float a[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = c0 + e;
+            const int k = c < p.h0 ? 0 : (c < p.h01 ? 1 : 2);
+            a[e] = __double2float_rn(pos[k] * lomega[c]);
+        }
+        uint32_t cw[4], sw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            cossin_pair(a[2 * q], a[2 * q + 1], cw[q], sw[q]);
+        const v4u cv = v4u{cw[0], cw[1], cw[2], cw[3]}, sv = v4u{sw[0], sw[1], sw[2], sw[3]};
+        const int64_t o = (int64_t)row * p.R + c0;
+        *reinterpret_cast<v4u *>(p.cos + o) = cv;
+        *reinterpret_cast<v4u *>(p.cos + o + half) = cv;
+        *reinterpret_cast<v4u *>(p.sin + o) = sv;
+        *reinterpret_cast<v4u *>(p.sin + o + half) = sv;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // (a2, a3) rotate-half RoPE with tail passthrough     [ERNIE-fuse §2]
 //
 // A workgroup owns one view and tok_per_wg consecutive tokens (table rows
@@ -713,6 +774,16 @@ hipError_t launch_rope_cossin(const CosSinParams &params, hipStream_t stream)
         hipLaunchKernelGGL(rope_cossin_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, p);
     else
         hipLaunchKernelGGL(rope_cossin_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_cossin_grid(const CosSinGridParams &p, hipStream_t stream)
+{
+    uint32_t blocks = (p.groups_total + kThreads - 1) / kThreads;
+    if (blocks > 2048)
+        blocks = 2048;
+    const size_t lds = (size_t)(p.R / 2) * sizeof(double);
+    hipLaunchKernelGGL(rope_cossin_grid_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
     return hipGetLastError();
 }
 

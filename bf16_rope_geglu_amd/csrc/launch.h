@@ -67,6 +67,25 @@ struct CosSinParams {
     FastDiv div_s;         // row -> (b, s)
 };
 
+constexpr int kGridOmegaArgs = 256;  // half-column frequencies carried in the kernel arguments
+
+struct CosSinGridParams {
+    const int32_t *t_offset;   // per batch row, or null
+    uint16_t *cos;
+    uint16_t *sin;
+    double theta;
+    uint32_t groups_total;     // B * S * (R / 16): lanes of 8 half-columns
+    int32_t R;
+    int32_t h0, h01;           // d0/2 and (d0 + d1)/2: first half-column of axes 1 and 2
+    int32_t d[3];
+    FastDiv div_groups;        // divisor R / 16: lane -> (row, group)
+    FastDiv div_s;             // row -> (b, s)
+    FastDiv div_hw;            // s -> (t, h*Wg + w)
+    FastDiv div_w;             // h*Wg + w -> (h, w)
+    int32_t host_omega;        // 1: omega[] holds theta^(-2i/d_k) for every half-column
+    double omega[kGridOmegaArgs];
+};
+
 struct GegluParams {
     const uint16_t *in;
     uint16_t *out;
@@ -78,6 +97,7 @@ struct GegluParams {
 
 // Launchers: enqueue on `stream`, return the hipError_t of the launch.
 hipError_t launch_rope_cossin(const CosSinParams &p, hipStream_t stream);
+hipError_t launch_rope_cossin_grid(const CosSinGridParams &p, hipStream_t stream);
 hipError_t launch_rope_rotate_half(const RopeParams &p, hipStream_t stream);
 hipError_t launch_gelu_and_mul(const GegluParams &p, int grid, hipStream_t stream);
 hipError_t launch_build_gelu_table(hipStream_t stream);

@@ -77,6 +77,34 @@ RGG_API int rope_cossin_precompute(const float *freqs, int64_t S, int64_t B, int
                            uint16_t *cos_out, uint16_t *sin_out, hipStream_t stream);
 
 /*
+ * (a1, from positions) Rotary tables straight from a 3-axis token grid.
+ *                            [ERNIE-fuse §1, the angles the table hoist is fed]
+ *
+ * The same tables as rope_cossin_precompute, for the angles a 3-axis
+ * positional embedding gives a (T, Hg, Wg) grid of S = T*Hg*Wg tokens, with
+ * no fp32 angle tensor in memory.  The page names that embedding (EmbedND3)
+ * without defining it; the reading implemented here:
+ *   - token s sits at (t, h, w), s = (t*Hg + h)*Wg + w; batch row b shifts t
+ *     by t_offset[b] (t_offset == NULL: no shift);
+ *   - axis k (k = 0: t, 1: h, 2: w) owns d_k rotary columns and contributes
+ *     d_k/2 half-angles pos_k * theta^(-2i/d_k), i = 0 .. d_k/2 - 1;
+ *   - the half-angles of axes 0, 1, 2 in that order form f (R/2 values,
+ *     R = d0 + d1 + d2), and the angle row is cat(f, f);
+ *   - each half-angle is formed in double and rounded once to fp32 (the
+ *     angle rope_cossin_precompute would be given), and the tables hold its
+ *     correctly rounded bf16 cosine/sine, row b*S + s.
+ *
+ * Requirements: B, T, Hg, Wg >= 0; d0, d1, d2 >= 0 and even; theta > 0 and
+ * finite; R a multiple of 16 and at most 8192 (RGG_ERR_UNSUPPORTED
+ * otherwise); t_offset NULL or a 4-byte aligned device array of B int32;
+ * cos_out, sin_out 16-byte aligned device (B*S, R) bf16 tables that overlap
+ * neither each other nor t_offset.  Any of B, T, Hg, Wg or R zero: no work.
+ */
+RGG_API int rope_cossin_from_grid(int64_t B, int64_t T, int64_t Hg, int64_t Wg, int32_t d0,
+                                  int32_t d1, int32_t d2, double theta, const int32_t *t_offset,
+                                  uint16_t *cos_out, uint16_t *sin_out, hipStream_t stream);
+
+/*
  * One strided (B, S, H, D) bf16 tensor to rotate and where to put the result.
  * Element (b, s, h, d) of the input is x[b*x_stride_b + s*x_stride_s +
  * h*x_stride_h + d]; the output uses the out_* strides the same way.  A view

@@ -40,8 +40,9 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = declared_functions()
-    assert set(names) == {"rope_cossin_precompute", "rope_rotate_half_bf16", "gelu_and_mul_bf16",
-                          "rgg_prepare_device", "rgg_status_string"}
+    assert set(names) == {"rope_cossin_precompute", "rope_cossin_from_grid",
+                          "rope_rotate_half_bf16", "gelu_and_mul_bf16", "rgg_prepare_device",
+                          "rgg_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", rgg.LIBRARY], capture_output=True,
@@ -75,6 +76,29 @@ def test_cossin_checks(lib):
     assert cossin(lib, S=0) == OK
     assert cossin(lib, B=0, freqs=None) == OK
     assert cossin(lib, R=0) == OK
+
+
+def grid(lib, B=2, T=1, Hg=4, Wg=4, d=(4, 6, 6), theta=1e4, off=None, cos=A, sin=A + 8192):
+    return lib.rope_cossin_from_grid(B, T, Hg, Wg, *d, theta, off, cos, sin, None)
+
+
+def test_grid_checks(lib):
+    assert grid(lib, cos=None) == NULL
+    assert grid(lib, B=-1) == SHAPE
+    assert grid(lib, d=(4, 5, 7)) == SHAPE           # odd axis width
+    assert grid(lib, d=(-2, 6, 12)) == SHAPE
+    assert grid(lib, theta=0.0) == SHAPE
+    assert grid(lib, theta=float("inf")) == SHAPE
+    assert grid(lib, theta=float("nan")) == SHAPE
+    assert grid(lib, d=(4, 6, 2)) == UNSUPPORTED     # R = 12
+    assert grid(lib, d=(4096, 4096, 16)) == UNSUPPORTED  # R > 8192
+    assert grid(lib, cos=A + 2) == ALIGN
+    assert grid(lib, off=A + 1 + (1 << 20)) == ALIGN
+    assert grid(lib, sin=A + 16) == ALIAS            # tables overlap
+    assert grid(lib, off=A + 64) == ALIAS            # offsets inside a table
+    assert grid(lib, T=0) == OK
+    assert grid(lib, B=0, cos=None) == OK
+    assert grid(lib, d=(0, 0, 0)) == OK
 
 
 def view(x=A, out=A + (1 << 24), xs=(8192, 1024, 128), os_=(8192, 1024, 128)):
@@ -202,4 +226,5 @@ def test_stream_reference_loads_and_checks_arguments():
     assert ref.rgg_stream_ref(A, None, A + 4096, 0, 256, None) == 2
     assert ref.rgg_stream_ref(A, None, A + 4096, 16, 96, None) == 2
     assert ref.rgg_stream_ref(A + 8, None, A + 4096, 16, 256, None) == 2
-    assert ref.rgg_stream_ref(None, None, A + 4096, 16, 256, None) == 2
+    assert ref.rgg_stream_ref(None, A, A + 4096, 16, 256, None) == 2
+    assert ref.rgg_stream_ref(A, None, None, 16, 256, None) == 2

@@ -172,6 +172,53 @@ def test_cossin_empty_and_guards(orc):
 
 
 # ---------------------------------------------------------------------------
+# (a1, from positions) cos/sin tables of a 3-axis token grid
+# ---------------------------------------------------------------------------
+
+GRID_TABLES = [  # B, grid, dims, theta, t_offset
+    (1, (1, 64, 64), (32, 48, 48), 1e4, None),       # rope_qk
+    (2, (1, 64, 64), (24, 36, 36), 1e4, None),       # partial
+    (4, (2, 64, 64), (32, 48, 48), 1e4, None),       # dit_layer
+    (3, (3, 7, 11), (16, 8, 8), 1e4, [0, 5, 1000]),  # ragged grid, per-batch shifts
+    (2, (5, 1, 9), (0, 16, 16), 256.0, [7, -3]),     # an axis with no columns
+    (1, (1, 2, 3), (2, 6, 8), 1e6, None),            # one 8-column group per row
+    (2, (2, 3, 5), (256, 256, 128), 1e4, [3, 0]),    # R = 640: frequencies built on the device
+]
+
+
+@pytest.mark.parametrize("case", GRID_TABLES, ids=lambda c: "B{}g{}x{}x{}d{}-{}-{}".format(
+    c[0], *c[1], *c[2]))
+def test_cossin_from_grid(orc, case):
+    B, grid, dims, theta, off = case
+    say(f"grid tables {case}")
+    T, Hg, Wg = grid
+    S, R = T * Hg * Wg, sum(dims)
+    offd = None if off is None else torch.tensor(off, dtype=torch.int32, device="cuda")
+    gc_t, gs_t = with_guards((B * S, R)), with_guards((B * S, R))
+    rgg.rope_cossin_from_grid(B, grid, dims, theta, offd, cos_out=gc_t[0], sin_out=gs_t[0])
+    gc_t[1]()
+    gs_t[1]()
+    gc, gs = host(gc_t[0]), host(gs_t[0])
+    angles = orc.rope_angles_grid(B, grid, dims, theta, off)
+    oc, os_ = orc.rope_cossin(angles)
+    assert_ulp_bar(gc, oc, "grid cos")
+    assert_ulp_bar(gs, os_, "grid sin")
+    # Same fp32 angles => the same bits as the precompute fed the oracle's angles.
+    pc, ps = gpu_cossin(angles)
+    assert_bitexact(gc, pc, "grid cos vs precompute of the oracle's angles")
+    assert_bitexact(gs, ps, "grid sin vs precompute of the oracle's angles")
+
+
+def test_cossin_from_grid_empty():
+    say("grid tables, empty shapes")
+    c, s_ = rgg.rope_cossin_from_grid(0, (1, 4, 4), (4, 6, 6))
+    assert c.shape == (0, 16) and s_.shape == (0, 16)
+    c, s_ = rgg.rope_cossin_from_grid(2, (1, 0, 4), (4, 6, 6))
+    assert c.shape == (0, 16)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
 # (a2, a3) rotate-half RoPE
 # ---------------------------------------------------------------------------
 

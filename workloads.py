@@ -192,6 +192,7 @@ def algo_bytes(wid):
         r = w["rope"]
         T = r["B"] * r["S"]
         out["precompute"] = T * r["R"] * 4 + 2 * T * r["R"] * 2
+        out["precompute_grid"] = 2 * T * r["R"] * 2
         x = r["views"] * T * r["H"] * r["D"] * 2
         out["rope"] = 2 * x + 2 * T * r["R"] * 2
     if "geglu" in w:
