@@ -662,6 +662,50 @@ print("ok", flush=True)
     assert "status 7" in r.stdout and "ok" in r.stdout
 
 
+def test_first_gelu_calls_from_several_threads(orc):
+    """In a fresh process, four host threads make their first GEGLU call at
+    once, each on its own stream: the one-time table build is serialized and
+    waited for, so every thread's result is right."""
+    import subprocess
+    import sys
+    code = r"""
+import sys, threading
+sys.path.insert(0, %r)
+import numpy as np
+import torch
+import bf16_rope_geglu_amd as rgg
+import workloads as W
+N = 4
+inps = [W.normal_bf16((512, 2 * 1024), 9100 + k, 2.0) for k in range(N)]
+dev = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in inps]
+outs = [None] * N
+streams = [torch.cuda.Stream() for _ in range(N)]
+torch.cuda.synchronize()
+go = threading.Barrier(N)
+def work(k):
+    with torch.cuda.stream(streams[k]):
+        go.wait()
+        outs[k] = rgg.gelu_and_mul_bf16(dev[k])
+threads = [threading.Thread(target=work, args=(k,)) for k in range(N)]
+for t in threads: t.start()
+for t in threads: t.join()
+torch.cuda.synchronize()
+for k in range(N):
+    np.save(sys.argv[1] + "/out%%d.npy" %% k, outs[k].view(torch.int16).cpu().numpy().view(np.uint16))
+print("ok", flush=True)
+""" % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        r = subprocess.run([sys.executable, "-c", code, d], capture_output=True, text=True,
+                           timeout=240)
+        say(r.stdout.strip(), r.stderr.strip()[-500:])
+        assert r.returncode == 0 and "ok" in r.stdout
+        for k in range(4):
+            inp = W.normal_bf16((512, 2 * 1024), 9100 + k, 2.0)
+            got = np.load(os.path.join(d, f"out{k}.npy"))
+            assert_ulp_bar(got, orc.gelu_and_mul(inp), f"thread {k}")
+
+
 # ---------------------------------------------------------------------------
 # The C ABI from plain C: tests/host/capi_client.c, no Python in between
 # ---------------------------------------------------------------------------
