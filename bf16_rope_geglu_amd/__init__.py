@@ -65,10 +65,12 @@ def library():
                                               _I, _I, _P, _P, _P]
         lib.gelu_and_mul_bf16.argtypes = [_P, _I, _I, _I, _P, _I, _P]
         lib.rgg_prepare_device.argtypes = [ctypes.c_int]
+        lib.rgg_selfcheck.argtypes = [_P, _I, _P, ctypes.POINTER(ctypes.c_uint32)]
         lib.rgg_status_string.argtypes = [ctypes.c_int]
         lib.rgg_status_string.restype = ctypes.c_char_p
         for f in (lib.rope_cossin_precompute, lib.rope_cossin_from_grid,
-                  lib.rope_rotate_half_bf16, lib.gelu_and_mul_bf16, lib.rgg_prepare_device):
+                  lib.rope_rotate_half_bf16, lib.gelu_and_mul_bf16, lib.rgg_prepare_device,
+                  lib.rgg_selfcheck):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -226,6 +228,26 @@ def prepare_device(device=None):
     """Build the constant GELU table on `device` now (before graph capture)."""
     idx = torch.cuda.current_device() if device is None else torch.device(device).index
     _check("rgg_prepare_device", library().rgg_prepare_device(idx))
+
+
+SELFCHECK_WORKSPACE_BYTES = 1 << 20
+_SELFCHECK_FAILED = 8
+
+
+def selfcheck(device=None):
+    """Run the device self-check on `device` (default: current) on the current
+    stream; returns the mask of failed checks (0 when every result has its
+    expected bits).  Raises RggError for any other error."""
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None
+                       else torch.device(device).index)
+    ws = torch.empty(SELFCHECK_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    failed = ctypes.c_uint32(0)
+    with torch.cuda.device(dev):
+        status = library().rgg_selfcheck(ws.data_ptr(), ws.numel(), _stream(dev),
+                                         ctypes.byref(failed))
+    if status not in (0, _SELFCHECK_FAILED):
+        _check("rgg_selfcheck", status)
+    return failed.value
 
 
 # The page's own names ---------------------------------------------------------

@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(HERE, "lib")
 LIBRARY = os.path.join(LIBDIR, "librgg.so")
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "capi.cpp")]
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "capi.cpp"),
+           os.path.join(CSRC, "selfcheck.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -111,6 +111,8 @@ const char *rgg_status_string(int status)
     case RGG_ERR_CAPTURING:
         return "GELU table not built on this device and the stream is capturing; "
                "call rgg_prepare_device first";
+    case RGG_ERR_SELFCHECK:
+        return "device self-check: a result differs from its expected bits";
     default:
         return "unknown status";
     }

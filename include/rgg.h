@@ -50,8 +50,10 @@ typedef enum rgg_status {
     RGG_ERR_ALIAS = 5,       /* an output overlaps an input or another output (other than
                                 the exact in-place forms each call allows) */
     RGG_ERR_HIP = 6,         /* the HIP runtime reported an error */
-    RGG_ERR_CAPTURING = 7    /* first GEGLU call on a device made while `stream` is being
+    RGG_ERR_CAPTURING = 7,   /* first GEGLU call on a device made while `stream` is being
                                 captured: call rgg_prepare_device() before capturing */
+    RGG_ERR_SELFCHECK = 8    /* rgg_selfcheck found a result that differs from its
+                                expected bits */
 } rgg_status;
 
 /*
@@ -178,6 +180,38 @@ RGG_API int gelu_and_mul_bf16(const uint16_t *input, int64_t rows, int64_t hidde
  * unchanged.
  */
 RGG_API int rgg_prepare_device(int device);
+
+/*
+ * Device self-check: the bit-exactness gate of the fused path, run on the
+ * caller's device and stream against expected bits derived by hand from the
+ * definitions (no eager twin to compare with).
+ *                                   [ERNIE-fuse §3, its bit-exact fusion gate]
+ *
+ * Runs the entry points above on small inputs staged in `workspace` and
+ * compares on the host, bit for bit:
+ *   bit 0  cos/sin of the fp32 angles 0, -0, pi, pi/2, 2*pi, pi/3, pi/6, 100
+ *          against their correctly rounded bf16 values (50-digit evaluation);
+ *   bit 1  rotate-half on hand-derived worked vectors (ties to even after the
+ *          product, no fused multiply-add, subnormals kept, overflow, signed
+ *          zeros, different angles per half);
+ *   bit 2  rotate-half with a zero angle returns x (two heads, a tail), with
+ *          -0 becoming +0 in the rotated columns only;
+ *   bit 3  G at textbook points (x = 1, 2, -1, 0.5, 3, -2, -3, -5.5);
+ *   bit 4  G over all 65536 bf16 inputs against the rules that fix it outside
+ *          the tabulated range (G = x for x >= 16, -0 for x <= -16, x/2 for
+ *          2^-125 <= |x| < 2^-10, signed zeros, Inf and NaN) and its
+ *          monotonicity for x > 0;
+ *   bit 5  the multiply: up = 2 doubles every finite G below 2^127 exactly.
+ * `*failed` (if not NULL) receives the mask of failed checks.  Returns
+ * RGG_OK when every check passes, RGG_ERR_SELFCHECK otherwise.  Synchronous:
+ * waits for `stream`.  Not allowed while `stream` is capturing
+ * (RGG_ERR_CAPTURING).  `workspace` is caller-owned device memory of at
+ * least RGG_SELFCHECK_WORKSPACE_BYTES bytes, 256-byte aligned; its contents
+ * are overwritten.
+ */
+#define RGG_SELFCHECK_WORKSPACE_BYTES (1 << 20)
+RGG_API int rgg_selfcheck(void *workspace, int64_t workspace_bytes, hipStream_t stream,
+                          uint32_t *failed);
 
 /* Static, human-readable text for a status code (never NULL). */
 RGG_API const char *rgg_status_string(int status);

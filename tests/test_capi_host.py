@@ -20,7 +20,7 @@ import bf16_rope_geglu_amd as rgg
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rgg.h")
 
-OK, NULL, SHAPE, UNSUPPORTED, ALIGN, ALIAS, HIP, CAPTURING = range(8)
+OK, NULL, SHAPE, UNSUPPORTED, ALIGN, ALIAS, HIP, CAPTURING, SELFCHECK = range(9)
 A = 0x7F0000000000  # a 16-byte aligned fake device address
 
 
@@ -42,7 +42,7 @@ def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) == {"rope_cossin_precompute", "rope_cossin_from_grid",
                           "rope_rotate_half_bf16", "gelu_and_mul_bf16", "rgg_prepare_device",
-                          "rgg_status_string"}
+                          "rgg_selfcheck", "rgg_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", rgg.LIBRARY], capture_output=True,
@@ -52,7 +52,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = lib.rgg_status_string(code)
         assert s and s.decode() != "unknown status"
     assert lib.rgg_status_string(99).decode() == "unknown status"
@@ -228,3 +228,53 @@ def test_stream_reference_loads_and_checks_arguments():
     assert ref.rgg_stream_ref(A + 8, None, A + 4096, 16, 256, None) == 2
     assert ref.rgg_stream_ref(None, A, A + 4096, 16, 256, None) == 2
     assert ref.rgg_stream_ref(A, None, None, 16, 256, None) == 2
+
+
+def test_selfcheck_argument_checks(lib):
+    """Refused before any device work: no workspace, too small, misaligned."""
+    import ctypes
+    failed = ctypes.c_uint32(5)
+    assert lib.rgg_selfcheck(None, 1 << 20, None, ctypes.byref(failed)) == NULL
+    assert failed.value == 0
+    assert lib.rgg_selfcheck(A, (1 << 20) - 1, None, None) == SHAPE
+    assert lib.rgg_selfcheck(A + 128, 1 << 20, None, None) == ALIGN
+
+
+def _c_array(text, name):
+    body = re.search(name + r"\[[^=]*=\s*\{(.*?)\};", text, re.S).group(1)
+    body = re.sub(r"//[^\n]*", "", body)
+    return [int(v, 16) for v in re.findall(r"0x([0-9A-Fa-f]+)", body)]
+
+
+def test_selfcheck_expected_values_agree_with_oracle_and_mpmath():
+    """The self-check's expected bits (hand-derived in selfcheck.cpp) agree
+    with the pinned oracle and with 50-digit cos/sin, so a typo there is
+    caught without a GPU."""
+    import mpmath
+    import numpy as np
+
+    import oracle
+    o = oracle.get()
+    with open(os.path.join(ROOT, "bf16_rope_geglu_amd", "csrc", "selfcheck.cpp")) as f:
+        text = f.read()
+    angles = np.array(_c_array(text, "kAngles"), np.uint32).view(np.float32)
+    cos, sin = _c_array(text, "kCos"), _c_array(text, "kSin")
+    oc, os_ = o.rope_cossin(angles.reshape(1, 1, 1, 8))
+    assert oc.ravel().tolist() == cos and os_.ravel().tolist() == sin
+    mpmath.mp.dps = 50
+    for a, c, s_ in zip(angles, cos, sin):
+        for fn, bits in ((mpmath.cos, c), (mpmath.sin, s_)):
+            v = float(np.array([bits << 16], np.uint32).view(np.float32)[0])
+            exact = fn(mpmath.mpf(float(a)))
+            if v != 0:
+                step = 2.0 ** (int(np.floor(np.log2(abs(v)))) - 7)
+                assert abs(exact - v) <= step / 2
+    rope = np.array(_c_array(text, "kRope"), np.uint16).reshape(8, 8)
+    x = np.concatenate([rope[:, 0], rope[:, 1]]).reshape(1, 1, 1, 16)
+    cs = np.concatenate([rope[:, 2], rope[:, 4]]).reshape(1, 16)
+    sn = np.concatenate([rope[:, 3], rope[:, 5]]).reshape(1, 16)
+    out = o.rope_rotate_half(x, cs, sn).ravel()
+    assert out[:8].tolist() == rope[:, 6].tolist() and out[8:].tolist() == rope[:, 7].tolist()
+    gel = np.array(_c_array(text, "kGelu"), np.uint16).reshape(8, 2)
+    for g, want in gel:
+        assert o.gelu_bf16(int(g)) == want

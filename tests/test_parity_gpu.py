@@ -99,7 +99,7 @@ def with_guards(shape, fill=0x7FC1):
 # ---------------------------------------------------------------------------
 
 def gpu_cossin(freqs_np):
-    f = torch.from_numpy(np.ascontiguousarray(freqs_np)).cuda()
+    f = torch.from_numpy(np.array(freqs_np, dtype=np.float32, order="C", copy=True)).cuda()
     c, s = rgg.rope_cossin_precompute(f)
     return host(c), host(s)
 
@@ -704,6 +704,30 @@ print("ok", flush=True)
             inp = W.normal_bf16((512, 2 * 1024), 9100 + k, 2.0)
             got = np.load(os.path.join(d, f"out{k}.npy"))
             assert_ulp_bar(got, orc.gelu_and_mul(inp), f"thread {k}")
+
+
+def test_selfcheck_passes():
+    """The library's own bit-exactness gate passes on this device, on the
+    default stream and on a side stream, twice in a row."""
+    say("selfcheck")
+    assert rgg.selfcheck() == 0
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert rgg.selfcheck() == 0
+    torch.cuda.synchronize()
+
+
+def test_selfcheck_refused_while_capturing():
+    say("selfcheck under capture")
+    rgg.prepare_device(0)
+    ws = torch.empty(rgg.SELFCHECK_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    status = None
+    with torch.cuda.graph(g):
+        status = rgg.library().rgg_selfcheck(
+            ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream, None)
+    assert status == 7
+    torch.cuda.synchronize()
 
 
 # ---------------------------------------------------------------------------
