@@ -37,6 +37,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -255,7 +256,10 @@ def run_sweep(reps=40, touch=2 << 30):
                     xs = [W.device_normal_bf16((B, S, H, D), 100 + 4 * k + v, device=dev)
                           for v in range(r["views"])]
                 outs = [torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev) for _ in xs]
-                sets.append((freqs, cos, sin, xs, outs))
+                # the attention consumer's head-major layout, written through strides
+                bhsd = [torch.empty((B, H, S, D), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
+                        for _ in xs] if r["layout"] == "qkv" else None
+                sets.append((freqs, cos, sin, xs, outs, bhsd))
             pre = [(lambda st=st: rgg.rope_cossin_precompute(st[0], st[1], st[2])) for st in sets]
             rot = [(lambda st=st: rgg.rope_rotate_half_bf16(st[3], st[1], st[2], out=st[4]))
                    for st in sets]
@@ -267,6 +271,13 @@ def run_sweep(reps=40, touch=2 << 30):
                     for st in sets]
                 steps.append(("rope_cossin_from_grid", "precompute_grid", grd, 0))
             steps.append(("rope_rotate_half_bf16", "rope", rot, 1))
+            if r["layout"] == "qkv":
+                inplace = [(lambda st=st: rgg.rope_rotate_half_bf16(st[3], st[1], st[2], out=st[3]))
+                           for st in sets]
+                to_bhsd = [(lambda st=st: rgg.rope_rotate_half_bf16(st[3], st[1], st[2], out=st[5]))
+                           for st in sets]
+                steps.append(("rope_rotate_half_bf16, in place in qkv", "rope", inplace, 1))
+                steps.append(("rope_rotate_half_bf16, into (B, H, S, D)", "rope", to_bhsd, 1))
             for name, key, fns, reads in steps:
                 us, gbps = timed(fns, algo[key])
                 rows_out.append((wl["name"], name, algo[key], nsets, us, gbps,
@@ -362,12 +373,16 @@ def _per_dispatch(rows, counter, symbol):
     return sorted(vals.values())
 
 
+KNOWN_KERNELS = ("rope_cossin_kernel", "rope_cossin_grid_kernel", "rope_rotate_half_kernel",
+                 "rope_rotate_half_lane_kernel", "gelu_and_mul_kernel", "build_gelu_table_kernel",
+                 "stream_ref_kernel")
+
+
 def _short_kernel(name):
-    for v in KERNEL_SYMBOL.values():
-        if v in name:
-            return v
-    for v in ("build_gelu_table_kernel", "stream_ref_kernel"):
-        if v in name:
+    """The kernel's own name inside a demangled symbol such as
+    `rgg::(anonymous namespace)::rope_rotate_half_kernel<true, true>(...)`."""
+    for v in KNOWN_KERNELS:
+        if re.search(r"(?:^|::|\s)" + v + r"\s*[<(]", name):
             return v
     return None
 
@@ -395,19 +410,16 @@ def trace_summary(d, out, command):
             trace.extend(csv.DictReader(f))
     trace = [r for r in trace if _short_kernel(r["Kernel_Name"])]
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
-    runs = []
+    groups = {}
     for r in trace:
         key = (_short_kernel(r["Kernel_Name"]), r["Grid_Size_X"], r["Workgroup_Size_X"])
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        if runs and runs[-1][0] == key:
-            runs[-1][1].append(dur)
-        else:
-            runs.append((key, [dur]))
-    if runs:
-        lines += ["Dispatch durations, consecutive runs in launch order:", "",
+        groups.setdefault(key, []).append(dur)
+    if groups:
+        lines += ["Dispatch durations per kernel and launch shape, in order of first launch:", "",
                   "| kernel | grid threads | workgroup | dispatches | median us | min us |",
                   "|---|---|---|---|---|---|"]
-        for (k, g, w), ds in runs:
+        for (k, g, w), ds in groups.items():
             ds.sort()
             lines.append(f"| {k} | {g} | {w} | {len(ds)} | {ds[len(ds) // 2]:.2f} | {ds[0]:.2f} |")
         lines.append("")
