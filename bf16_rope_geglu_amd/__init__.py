@@ -23,8 +23,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "lib", "librgg.so")
 
 __all__ = [
-    "rope_cossin_precompute", "rope_rotate_half_bf16", "gelu_and_mul_bf16", "prepare_device",
-    "RggError", "library", "precompute_rope_cos_sin", "fused_rope_rotate_half_bitexact",
+    "rope_cossin_precompute", "rope_cossin_from_grid", "rope_rotate_half_bf16",
+    "gelu_and_mul_bf16", "prepare_device", "selfcheck", "RggError", "library",
+    "precompute_rope_cos_sin", "fused_rope_rotate_half_bitexact",
     "gelu_and_mul_with_activation_rounding",
 ]
 
@@ -90,6 +91,13 @@ def _need(t, dtype, name):
         raise TypeError(f"{name} must be a {dtype} tensor on a HIP device")
 
 
+def _one_device(dev, **tensors):
+    """Every tensor of one call must live on the device the call runs on."""
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the call runs on {dev}")
+
+
 def rope_cossin_precompute(freqs, cos_out=None, sin_out=None):
     """(S, B, 1, R) fp32 angles -> (cos, sin), each bf16 (B*S, R), row b*S + s.
 
@@ -110,6 +118,7 @@ def rope_cossin_precompute(freqs, cos_out=None, sin_out=None):
             raise ValueError(f"{name} must be contiguous ({B * S}, {R})")
     if R > 0 and freqs.numel() > 0 and freqs.stride(3) != 1:
         raise ValueError("freqs needs unit stride along its last dimension")
+    _one_device(dev, cos_out=cos_out, sin_out=sin_out)
     with torch.cuda.device(dev):
         _check("rope_cossin_precompute", library().rope_cossin_precompute(
             freqs.data_ptr(), S, B, R, freqs.stride(0), freqs.stride(1),
@@ -126,8 +135,19 @@ def rope_cossin_from_grid(B, grid, dims, theta=10000.0, t_offset=None, cos_out=N
     T, Hg, Wg = (int(v) for v in grid)
     d0, d1, d2 = (int(v) for v in dims)
     S, R = T * Hg * Wg, d0 + d1 + d2
-    dev = torch.device(device) if device is not None else (
-        t_offset.device if t_offset is not None else torch.device("cuda", torch.cuda.current_device()))
+    for name, t in (("cos_out", cos_out), ("sin_out", sin_out)):
+        if t is not None:
+            _need(t, torch.bfloat16, name)
+    if t_offset is not None:
+        _need(t_offset, torch.int32, "t_offset")
+    if device is not None:
+        dev = torch.device(device)
+    elif cos_out is not None:
+        dev = cos_out.device
+    elif t_offset is not None:
+        dev = t_offset.device
+    else:
+        dev = torch.device("cuda", torch.cuda.current_device())
     if cos_out is None:
         cos_out = torch.empty((B * S, R), dtype=torch.bfloat16, device=dev)
     if sin_out is None:
@@ -136,9 +156,9 @@ def rope_cossin_from_grid(B, grid, dims, theta=10000.0, t_offset=None, cos_out=N
         _need(t, torch.bfloat16, name)
         if tuple(t.shape) != (B * S, R) or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous ({B * S}, {R})")
+    _one_device(dev, cos_out=cos_out, sin_out=sin_out, t_offset=t_offset)
     off = None
     if t_offset is not None:
-        _need(t_offset, torch.int32, "t_offset")
         if tuple(t_offset.shape) != (B,) or not t_offset.is_contiguous():
             raise ValueError(f"t_offset must be a contiguous ({B},) int32 tensor")
         off = t_offset.data_ptr()
@@ -186,6 +206,8 @@ def rope_rotate_half_bf16(x, cos, sin, out=None):
         views[v] = RopeView(xv.data_ptr(), ov.data_ptr(), xv.stride(0), xv.stride(1),
                             xv.stride(2), ov.stride(0), ov.stride(1), ov.stride(2))
     dev = xs[0].device
+    _one_device(dev, cos=cos, sin=sin, **{f"x[{v}]": t for v, t in enumerate(xs)},
+                **{f"out[{v}]": t for v, t in enumerate(outs)})
     with torch.cuda.device(dev):
         _check("rope_rotate_half_bf16", library().rope_rotate_half_bf16(
             views, len(xs), B, S, H, D, R, cos.data_ptr(), sin.data_ptr(), _stream(dev)))
@@ -217,6 +239,7 @@ def gelu_and_mul_bf16(input, out=None):
         raise ValueError("out needs unit stride along its last dimension")
     rows = inp2.shape[0]
     dev = input.device
+    _one_device(dev, out=out)
     with torch.cuda.device(dev):
         _check("gelu_and_mul_bf16", library().gelu_and_mul_bf16(
             inp2.data_ptr(), rows, hidden, inp2.stride(0) if rows else 2 * hidden,

@@ -196,6 +196,9 @@ def test_binding_rejects_host_tensors():
         rgg.gelu_and_mul_bf16(torch.zeros(4, 16, dtype=torch.bfloat16))
     with pytest.raises(TypeError):
         rgg.rope_cossin_precompute(torch.zeros(4, 1, 1, 16))
+    tab = torch.zeros(2 * 16, 16, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        rgg.rope_cossin_from_grid(2, (1, 4, 4), (4, 6, 6), cos_out=tab, sin_out=tab.clone())
 
 
 def test_binding_error_carries_status(lib):
