@@ -298,6 +298,106 @@ def test_rope_adversarial(orc, case):
         assert_bitexact(host(guarded[v][0]), oracle_rope(orc, xs[v], cos, sin), f"view {v}")
 
 
+def _rope_fuzz_case(k):
+    """A seeded random RoPE configuration; k % 4 steers it towards one launch
+    path: 0 one vector per lane (wide rows, R/2 splitting lines, aligned),
+    1 two-vector items on whole lines, 2 several tokens per workgroup,
+    3 arbitrary 8-element strides."""
+    rng = np.random.Generator(np.random.PCG64(7700 + k))
+    kind = k % 4
+    if kind == 0:
+        D = int(rng.choice([128, 256, 512]))
+        H = int(rng.integers(2112 // D + 1, 4096 // D + 1))
+        R = int(rng.choice([r for r in range(16, D + 1, 16) if r % 64]))
+        align = 64
+    elif kind == 1:
+        D = int(rng.choice([64, 128, 256]))
+        H = int(rng.integers(2048 // D + 1, 40))
+        R = int(rng.choice([r for r in range(64, D + 1, 64)]))
+        align = 64
+    elif kind == 2:
+        D = int(rng.choice([16, 32, 48, 64, 128]))
+        H = int(rng.integers(1, 9))
+        R = int(rng.choice(range(0, D + 1, 16)))
+        align = 8
+    else:
+        D = int(rng.choice([8 * i for i in range(1, 33)]))
+        H = int(rng.integers(1, 24))
+        R = int(rng.choice(range(0, D + 1, 16)))
+        align = 8
+    B, S = int(rng.integers(1, 4)), int(rng.integers(1, 40))
+    nv = int(rng.integers(1, 5))
+    views = []
+    for v in range(nv):
+        def strides():
+            sh = D + align * int(rng.integers(0, 3))
+            ss = H * sh + align * int(rng.integers(0, 3))
+            sb = S * ss + align * int(rng.integers(0, 3))
+            return sb, ss, sh, align * int(rng.integers(0, 4))
+        xs = strides()
+        in_place = kind != 0 and rng.random() < 0.25
+        views.append((xs, None if in_place else strides()))
+    return B, S, H, D, R, views, int(rng.integers(0, 1 << 30))
+
+
+def _strided(buf, off, st, shape):
+    return torch.as_strided(buf, shape, (st[0], st[1], st[2], 1), off)
+
+
+@pytest.mark.parametrize("k", range(48))
+def test_rope_random_layouts(orc, k):
+    """Seeded random shapes, strides, view counts and in-place views over
+    every launch path, element by element against the oracle, with the
+    padding between rows left untouched."""
+    B, S, H, D, R, views, seed = _rope_fuzz_case(k)
+    say(f"rope fuzz {k}: B{B} S{S} H{H} D{D} R{R} views {views}")
+    cos, sin = orc.rope_cossin(W.freqs_unpaired(S, B, R, seed)) if R else (
+        np.zeros((B * S, 0), np.uint16), np.zeros((B * S, 0), np.uint16))
+    sentinel = 0x7FC1
+    xs, outs, bufs = [], [], []
+    for v, (xst, ost) in enumerate(views):
+        n_x = (B - 1) * xst[0] + (S - 1) * xst[1] + (H - 1) * xst[2] + D + xst[3]
+        host_x = W.special_bf16((n_x,), seed + 1 + v)
+        xbuf = dev(host_x)
+        xv = _strided(xbuf, xst[3], xst, (B, S, H, D))
+        if ost is None:
+            ov, obuf = xv, None
+        else:
+            n_o = (B - 1) * ost[0] + (S - 1) * ost[1] + (H - 1) * ost[2] + D + ost[3]
+            obuf = torch.full((n_o,), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+            ov = _strided(obuf, ost[3], ost, (B, S, H, D))
+        xs.append(xv)
+        outs.append(ov)
+        bufs.append((host_x, xbuf, obuf))
+    rgg.rope_rotate_half_bf16(xs, dev(cos) if R else torch.empty((B * S, 0), dtype=torch.bfloat16,
+                                                                  device="cuda"),
+                              dev(sin) if R else torch.empty((B * S, 0), dtype=torch.bfloat16,
+                                                             device="cuda"), out=outs)
+    for v, ((xst, ost), (host_x, xbuf, obuf)) in enumerate(zip(views, bufs)):
+        x_in = np.lib.stride_tricks.as_strided(host_x[xst[3]:], (B, S, H, D),
+                                               tuple(2 * t for t in (xst[0], xst[1], xst[2], 1)))
+        want = orc.rope_rotate_half(np.ascontiguousarray(x_in), cos, sin)
+        if ost is None:                     # in place: the tail is left as it was
+            want[..., R:] = x_in[..., R:]
+            after = host(xbuf)
+            got = np.lib.stride_tricks.as_strided(after[xst[3]:], (B, S, H, D),
+                                                  tuple(2 * t for t in (xst[0], xst[1], xst[2], 1)))
+            touched = np.zeros(after.shape, bool)
+            np.lib.stride_tricks.as_strided(touched[xst[3]:], (B, S, H, D), tuple(
+                t for t in (xst[0], xst[1], xst[2], 1)))[...] = True
+            assert np.array_equal(after[~touched], host_x[~touched]), "wrote outside the view"
+        else:
+            after = host(obuf)
+            got = np.lib.stride_tricks.as_strided(after[ost[3]:], (B, S, H, D),
+                                                  tuple(2 * t for t in (ost[0], ost[1], ost[2], 1)))
+            touched = np.zeros(after.shape, bool)
+            np.lib.stride_tricks.as_strided(touched[ost[3]:], (B, S, H, D), tuple(
+                t for t in (ost[0], ost[1], ost[2], 1)))[...] = True
+            assert (after[~touched] == sentinel).all(), "wrote outside the output view"
+            assert np.array_equal(host(xbuf), host_x), "input modified"
+        assert_bitexact(np.ascontiguousarray(got), want, f"fuzz {k} view {v}")
+
+
 def make_qkv(B, S, H, D, seed):
     qkv = W.normal_bf16((B, S, 3 * H * D), seed)
     return qkv
@@ -475,6 +575,41 @@ def test_geglu_edge_shapes(orc, case):
     nan = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
     assert ((got[nan] & 0x7F80) == 0x7F80).all() and ((got[nan] & 0x7F) != 0).all()
     assert_ulp_bar(got[~nan], want[~nan], f"geglu {case}")
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_geglu_random_layouts(orc, k):
+    """Seeded random rows, widths, row strides and in-place calls against the
+    oracle, with the row padding left untouched."""
+    rng = np.random.Generator(np.random.PCG64(8800 + k))
+    rows = int(rng.integers(1, 700))
+    hidden = 8 * int(rng.integers(1, 129))
+    is_ = 2 * hidden + 8 * int(rng.integers(0, 5))
+    in_place = rng.random() < 0.3
+    os_ = is_ if in_place else hidden + 8 * int(rng.integers(0, 5))
+    say(f"geglu fuzz {k}: rows {rows} hidden {hidden} strides {is_}/{os_} in place {in_place}")
+    gen = W.special_bf16 if k % 2 else (lambda shape, seed: W.normal_bf16(shape, seed, 3.0))
+    full = gen((rows, is_), 8900 + k)
+    buf = dev(full)
+    inp = buf[:, :2 * hidden]
+    if in_place:
+        out_buf, out = buf, buf[:, :hidden]
+    else:
+        out_buf = torch.full((rows, os_), 0x7FC1, dtype=torch.int16,
+                             device="cuda").view(torch.bfloat16)
+        out = out_buf[:, :hidden]
+    rgg.gelu_and_mul_bf16(inp, out)
+    after = host(out_buf)
+    want = orc.gelu_and_mul(np.ascontiguousarray(full[:, :2 * hidden]))
+    got = after[:, :hidden]
+    if in_place:
+        assert np.array_equal(after[:, hidden:], full[:, hidden:]), "wrote past the gate half"
+    else:
+        assert (after[:, hidden:] == 0x7FC1).all(), "wrote into the row padding"
+        assert np.array_equal(host(buf), full), "input modified"
+    nan = ((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0)
+    assert ((got[nan] & 0x7F80) == 0x7F80).all() and ((got[nan] & 0x7F) != 0).all()
+    assert_ulp_bar(got[~nan], want[~nan], f"geglu fuzz {k}")
 
 
 def test_geglu_in_place_and_empty(orc):
