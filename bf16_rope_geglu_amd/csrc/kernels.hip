@@ -53,9 +53,6 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
 #ifndef RGG_ROPE_LANE
 #define RGG_ROPE_LANE 1          // one-token launches whose half-rotation splits 128-byte lines:
 #endif                           // one contiguous output vector per lane
-#ifndef RGG_ROPE_LANE_U2_MIN
-#define RGG_ROPE_LANE_U2_MIN 512 // one-vector lanes: two vectors per lane from this many per token
-#endif
 #ifndef RGG_ROPE_LDS
 #define RGG_ROPE_LDS 1           // 1: stage cos/sin rows in LDS; 0: read them per item
 #endif
@@ -799,9 +796,9 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
     p.wave_stage = RGG_ROPE_LDS && RGG_ROPE_WAVE_STAGE && p.tok_per_wg == 1 && wave_lds <= 65536;
     if (p.wave_stage)
         lds = wave_lds;
-    // Whole lines per instruction when each half (R bf16 = 2R bytes / 2) and
+    // Whole lines per instruction when each half (R/2 bf16 = R bytes) and
     // every row start are multiples of 128 bytes.
-    bool lines = p.R % 64 == 0;
+    bool lines = p.R % 128 == 0;
     for (int v = 0; v < p.n_views; ++v) {
         const RopeView &V = p.v[v];
         lines = lines && V.xs_h % 64 == 0 && V.os_h % 64 == 0 && V.xs_s % 64 == 0 &&
@@ -830,10 +827,7 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
         }
         if (whole) {
             p.div_vecs = make_fastdiv((uint32_t)(p.D / 8));
-            if ((int64_t)p.H * (p.D / 8) >= RGG_ROPE_LANE_U2_MIN)
-                kernel = rope_rotate_half_lane_kernel<true, 2>;
-            else
-                kernel = rope_rotate_half_lane_kernel<true, 1>;
+            kernel = rope_rotate_half_lane_kernel<true, 1>;
         }
     }
 #endif
