@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "launch.h"
 
 namespace rgg {
@@ -361,6 +363,22 @@ __device__ __forceinline__ void rope_token_base(const RopeParams &p, const RopeV
     ob = (int64_t)b * V.os_b + (int64_t)s * V.os_s;
 }
 
+// Workgroup -> (token chunk, view, part).  A token whose items fill several
+// workgroup passes is split over `parts` workgroups, each taking every
+// parts-th pass; consecutive workgroups walk the parts, then the views, then
+// the token chunks of this launch.
+__device__ __forceinline__ void rope_workgroup(const RopeParams &p, uint32_t &chunk, int &v,
+                                               int &part)
+{
+    const uint32_t wg = blockIdx.x;
+    const uint32_t q = fdiv(wg, p.div_vp);
+    const uint32_t rem = wg - q * (uint32_t)(p.n_views * p.parts);
+    const uint32_t vq = fdiv(rem, p.div_parts);
+    v = (int)vq;
+    part = (int)(rem - vq * (uint32_t)p.parts);
+    chunk = p.chunk0 + q;
+}
+
 // Item i of a workgroup whose first token is t0.  With OneToken the
 // workgroup holds a single token whose base offsets xb1/ob1 are uniform.
 template <bool OneToken>
@@ -409,9 +427,9 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
     float *lcos = reinterpret_cast<float *>(smem);  // [tpw][R]
     float *lsin = lcos + tpw * R;                   // [tpw][R]
 
-    const uint32_t wg = blockIdx.x;
-    const uint32_t wg_tok = p.chunk0 + fdiv(wg, p.div_views);
-    const int v = (int)(wg - (wg_tok - p.chunk0) * (uint32_t)p.n_views);
+    uint32_t wg_tok;
+    int v, part;
+    rope_workgroup(p, wg_tok, v, part);
     const int64_t t0 = (int64_t)wg_tok * tpw;
     const int ntok = (int)min((int64_t)tpw, p.tokens - t0);
     const RopeView V = p.v[v];
@@ -425,7 +443,8 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
         rope_token_base(p, V, (uint32_t)t0, xb1, ob1);
 
     constexpr int U = kRopeUnroll;
-    for (int base = 0; base < items; base += kRopeBlock * U) {
+    const int first = part * kRopeBlock * U;
+    for (int base = first; base < items; base += kRopeBlock * U * p.parts) {
         // Locate and load U items per lane before anything waits.  Lanes past
         // the end re-read the last item and tail items read their vector
         // twice, so no load sits under a branch.
@@ -439,7 +458,7 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
             x2[u] = load16<Nt>(V.x + it[u].xo + (it[u].rot ? half : 0));
         }
 #if RGG_ROPE_LDS
-        if (OneToken && p.wave_stage && base == 0) {
+        if (OneToken && p.wave_stage && base == first) {
             // One token: every wave stages its own fp32 copy of the row in
             // its own LDS slot, so no wave waits for another.  LDS operations
             // of one wave complete in order; the wave barrier keeps the
@@ -462,7 +481,7 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
         }
 #endif
 #if RGG_ROPE_LDS
-        if ((!OneToken || !p.wave_stage) && base == 0) {
+        if ((!OneToken || !p.wave_stage) && base == first) {
             // Stage this workgroup's cos/sin rows (consecutive table rows) as
             // fp32 while the x loads are in flight.
             const v4u *gc = reinterpret_cast<const v4u *>(p.cos + t0 * R);
@@ -540,9 +559,9 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int R = p.R, nv = p.D / 8, rv = R / 8, hv = R / 16;
-    const uint32_t wg = blockIdx.x;
-    const uint32_t t = p.chunk0 + fdiv(wg, p.div_views);
-    const int v = (int)(wg - (t - p.chunk0) * (uint32_t)p.n_views);
+    uint32_t t;
+    int v, part;
+    rope_workgroup(p, t, v, part);
     const RopeView V = p.v[v];
     int64_t xb, ob;
     rope_token_base(p, V, t, xb, ob);
@@ -550,7 +569,8 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     float *wc = reinterpret_cast<float *>(smem) + wave * 2 * R, *ws = wc + R;
 
-    for (int base = 0; base < items; base += kRopeBlock * U) {
+    const int first = part * kRopeBlock * U;
+    for (int base = first; base < items; base += kRopeBlock * U * p.parts) {
         int64_t oo[U];
         int j[U];
         v4u a[U], b[U];
@@ -565,7 +585,7 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
             a[u] = load16<Nt>(V.x + xo);
             b[u] = load16<false>(V.x + xo + pj * 8);
         }
-        if (base == 0) {
+        if (base == first) {
             const v4u *gc = reinterpret_cast<const v4u *>(p.cos + (int64_t)t * R);
             const v4u *gs = reinterpret_cast<const v4u *>(p.sin + (int64_t)t * R);
             for (int k = lane; k < R / 4; k += 64) {
@@ -804,6 +824,9 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
         lines = lines && V.xs_h % 64 == 0 && V.os_h % 64 == 0 && V.xs_s % 64 == 0 &&
                 V.os_s % 64 == 0 && ((uintptr_t)V.x & 127) == 0 && ((uintptr_t)V.out & 127) == 0;
     }
+    // Items of one token and view (the widest view decides), and how many a
+    // workgroup pass takes.
+    int64_t items = (int64_t)p.H * (p.tail_mask ? p.slots_tail : p.half / 8);
     void (*kernel)(RopeParams);
     if (p.tok_per_wg == 1 && lines)
         kernel = rope_rotate_half_kernel<true, true>;
@@ -828,19 +851,26 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
         if (whole) {
             p.div_vecs = make_fastdiv((uint32_t)(p.D / 8));
             kernel = rope_rotate_half_lane_kernel<true, 1>;
+            items = (int64_t)p.H * (p.D / 8);
         }
     }
 #endif
+    // A one-token workgroup whose token needs k >= 2 whole passes hands them
+    // to k workgroups instead (a partial last pass stays with the first).
+    p.parts = p.tok_per_wg == 1 ? (int32_t)std::max<int64_t>(1, items / (kRopeBlock * kRopeUnroll))
+                                : 1;
+    p.div_vp = make_fastdiv((uint32_t)(p.n_views * p.parts));
+    p.div_parts = make_fastdiv((uint32_t)p.parts);
     // A dispatch's grid is counted in 32-bit work-items, so very long token
     // ranges go out as several launches of at most kMaxRopeWorkgroups.
     const int64_t chunks = (p.tokens + p.tok_per_wg - 1) / p.tok_per_wg;
-    const int64_t per_launch = kMaxRopeWorkgroups / p.n_views;
+    const int64_t per_launch = kMaxRopeWorkgroups / (p.n_views * p.parts);
     for (int64_t c0 = 0; c0 < chunks; c0 += per_launch) {
         p.chunk0 = (uint32_t)c0;
         const int64_t n = chunks - c0 < per_launch ? chunks - c0 : per_launch;
         void *args[] = {&p};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel),
-                                       dim3((uint32_t)(n * p.n_views)), dim3(kRopeBlock), args,
+                                       dim3((uint32_t)(n * p.n_views * p.parts)), dim3(kRopeBlock), args,
                                        lds, stream);
         if (e == hipSuccess)
             e = hipGetLastError();

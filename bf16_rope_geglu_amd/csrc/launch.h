@@ -48,6 +48,9 @@ struct RopeParams {
     int32_t slots_tail;    // R/16 + (D - R)/8 work slots per head when the tail is copied
     int32_t wave_stage;    // one-token workgroups: each wave stages its own cos/sin row
     uint32_t chunk0;       // first token chunk of this launch (long ranges take several)
+    int32_t parts;         // workgroups per (token chunk, view)
+    FastDiv div_vp;        // divisor n_views * parts
+    FastDiv div_parts;     // divisor parts
     FastDiv div_s;         // token -> (b, s)
     FastDiv div_views;     // workgroup -> (token chunk, view)
     FastDiv div_heads;     // divisor H
