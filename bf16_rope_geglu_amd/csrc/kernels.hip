@@ -315,10 +315,15 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_grid_kernel(CosSinGridPa
 // cache lines) at once.  Each element is read and written by one lane, so
 // out == x is safe (the tail slots are then dropped).
 //
-// The lane issues its first item's loads before the workgroup stages the
-// fp32 cos/sin rows of its tokens in LDS, so the HBM latency overlaps the
-// staging and the barrier; every (head, slot) of a token then reuses the
-// staged row.
+// The lane issues its first item's loads before the cos/sin rows of its
+// tokens are staged as fp32 in LDS, so the HBM latency overlaps the staging;
+// every (head, slot) of a token then reuses the staged row.  A one-token
+// workgroup lets each wave stage its own copy (no workgroup barrier) while
+// the copies fit 64 KiB; otherwise the workgroup stages one copy behind a
+// barrier.  A token with k >= 2 whole passes of items is split over k
+// workgroups.  When R is not a multiple of 128 the two halves of a row split
+// cache lines between the two store instructions, and launches that allow it
+// use rope_rotate_half_lane_kernel below (one contiguous vector per lane).
 // ---------------------------------------------------------------------------
 
 // out1 = rne(rne(x1*c1) + rne(-x2*s1)), out2 = rne(rne(x2*c2) + rne(x1*s2)) on
