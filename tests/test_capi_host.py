@@ -281,3 +281,20 @@ def test_selfcheck_expected_values_agree_with_oracle_and_mpmath():
     gel = np.array(_c_array(text, "kGelu"), np.uint16).reshape(8, 2)
     for g, want in gel:
         assert o.gelu_bf16(int(g)) == want
+
+
+def test_cpu_baseline_leg_runs_on_a_small_sample():
+    """bench.py's cpu_baseline leg: the oracle on one thread and on all cores."""
+    import bench
+
+    out = bench.run_cpu_baseline(4, tokens=64, geglu_rows=16)
+    assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
+    assert out["all_cores"]["cores"] >= 1 and out["all_cores"]["value"] > 0
+
+
+def test_step_bytes_are_the_three_kernels():
+    """One dit_layer step moves 33.55 MB (tables) + 1090.52 MB (q and k RoPE)
+    + 1610.61 MB (GEGLU) algorithmically, and nothing else counts."""
+    import bench
+
+    assert bench.step_algo_bytes(4) == 33554432 + 1090519040 + 1610612736 == 2734686208
