@@ -55,6 +55,9 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
 #ifndef RGG_ROPE_LANE
 #define RGG_ROPE_LANE 1          // one-token launches whose half-rotation splits 128-byte lines:
 #endif                           // one contiguous output vector per lane
+#ifndef RGG_STAGE_FIRST
+#define RGG_STAGE_FIRST 1        // one-token RoPE, R <= 256: fetch the cos/sin row before x
+#endif
 #ifndef RGG_ROPE_LDS
 #define RGG_ROPE_LDS 1           // 1: stage cos/sin rows in LDS; 0: read them per item
 #endif
@@ -455,6 +458,19 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
         // twice, so no load sits under a branch.
         RopeItem it[U];
         v4u x1[U], x2[U];
+#if RGG_STAGE_FIRST
+        // With per-wave staging and R <= 256 each lane fetches at most one
+        // 16-byte vector of the cos/sin row, and it does so before its x
+        // loads: loads return in order, so waiting for the row then does not
+        // wait for x, and the LDS staging overlaps the HBM latency.
+        v4u stg = v4u{0u, 0u, 0u, 0u};
+        const bool stage1 = OneToken && p.wave_stage && R > 0 && R <= 256;
+        if (stage1 && base == first) {
+            const int k = min(tid & 63, R / 4 - 1);
+            const uint16_t *src = k >= R / 8 ? p.sin + t0 * R + (k - R / 8) * 8 : p.cos + t0 * R + k * 8;
+            stg = *reinterpret_cast<const v4u *>(src);
+        }
+#endif
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int ic = min(base + u * kRopeBlock + tid, items - 1);
@@ -472,6 +488,17 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
             float *wc = lcos + wave * 2 * R, *ws = wc + R;
             const v4u *gc = reinterpret_cast<const v4u *>(p.cos + t0 * R);
             const v4u *gs = reinterpret_cast<const v4u *>(p.sin + t0 * R);
+#if RGG_STAGE_FIRST
+            if (stage1) {
+                if (lane < R / 4) {
+                    const bool is_sin = lane >= R / 8;
+                    const int kk = is_sin ? lane - R / 8 : lane;
+                    float4 *d = reinterpret_cast<float4 *>((is_sin ? ws : wc) + kk * 8);
+                    d[0] = make_float4(bf_lo(stg.x), bf_hi(stg.x), bf_lo(stg.y), bf_hi(stg.y));
+                    d[1] = make_float4(bf_lo(stg.z), bf_hi(stg.z), bf_lo(stg.w), bf_hi(stg.w));
+                }
+            } else
+#endif
             for (int k = lane; k < R / 4; k += 64) {
                 const bool is_sin = k >= R / 8;
                 const int kk = is_sin ? k - R / 8 : k;
@@ -579,6 +606,16 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
         int64_t oo[U];
         int j[U];
         v4u a[U], b[U];
+#if RGG_STAGE_FIRST
+        v4u stg = v4u{0u, 0u, 0u, 0u};
+        const bool stage1 = R > 0 && R <= 256;
+        if (stage1 && base == first) {
+            const int k = min(lane, R / 4 - 1);
+            const uint16_t *src = k >= R / 8 ? p.sin + (int64_t)t * R + (k - R / 8) * 8
+                                             : p.cos + (int64_t)t * R + k * 8;
+            stg = *reinterpret_cast<const v4u *>(src);
+        }
+#endif
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int ic = min(base + u * kRopeBlock + tid, items - 1);
@@ -593,6 +630,17 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
         if (base == first) {
             const v4u *gc = reinterpret_cast<const v4u *>(p.cos + (int64_t)t * R);
             const v4u *gs = reinterpret_cast<const v4u *>(p.sin + (int64_t)t * R);
+#if RGG_STAGE_FIRST
+            if (stage1) {
+                if (lane < R / 4) {
+                    const bool is_sin = lane >= R / 8;
+                    const int kk = is_sin ? lane - R / 8 : lane;
+                    float4 *d = reinterpret_cast<float4 *>((is_sin ? ws : wc) + kk * 8);
+                    d[0] = make_float4(bf_lo(stg.x), bf_hi(stg.x), bf_lo(stg.y), bf_hi(stg.y));
+                    d[1] = make_float4(bf_lo(stg.z), bf_hi(stg.z), bf_lo(stg.w), bf_hi(stg.w));
+                }
+            } else
+#endif
             for (int k = lane; k < R / 4; k += 64) {
                 const bool is_sin = k >= R / 8;
                 const int kk = is_sin ? k - R / 8 : k;

@@ -442,6 +442,17 @@ def test_rope_partial_in_place_keeps_tail(orc):
     assert_bitexact(host(t), oracle_rope(orc, x, cos, sin), "in place with tail")
 
 
+def test_rope_zero_rotary_width_one_token(orc):
+    """R = 0 with one token per workgroup: the row copy only, with no cos/sin
+    row to fetch (regression: an early fetch of the row must not run)."""
+    say("rope R = 0, one token per workgroup")
+    B, S, H, D = 1, 3, 20, 240
+    x = W.special_bf16((B, S, H, D), 8700)
+    empty = torch.empty((B * S, 0), dtype=torch.bfloat16, device="cuda")
+    out = rgg.rope_rotate_half_bf16(dev(x), empty, empty)
+    assert_bitexact(host(out), x, "R = 0 copy")
+
+
 def test_rope_empty_shapes():
     say("rope empty shapes")
     c = torch.zeros((0, 16), dtype=torch.bfloat16, device="cuda")
