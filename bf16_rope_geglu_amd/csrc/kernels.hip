@@ -55,6 +55,9 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
 #ifndef RGG_ROPE_LANE
 #define RGG_ROPE_LANE 1          // one-token launches whose half-rotation splits 128-byte lines:
 #endif                           // one contiguous output vector per lane
+#ifndef RGG_GEGLU_LUT_FIRST
+#define RGG_GEGLU_LUT_FIRST 1    // GEGLU: fetch the lane's GELU-table vector before gate/up
+#endif
 #ifndef RGG_STAGE_FIRST
 #define RGG_STAGE_FIRST 1        // one-token RoPE, R <= 256: fetch the cos/sin row before x
 #endif
@@ -693,8 +696,9 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
 // path.  The multiply by up is exact in fp32 and rounded once.
 //
 // Layout of the work: one 16-byte vector (8 outputs) per lane.  The lane
-// issues its gate and up loads, then the workgroup copies the table into
-// LDS, so the table fill overlaps the HBM latency.
+// fetches its 16-byte share of the table (an L2 hit), then issues its gate
+// and up loads, then writes the table share to LDS: loads return in order,
+// so the table fill and the barrier overlap the HBM latency of gate and up.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kLutLo = 0x3A80u;                // bf16 bits of 2^-10
 constexpr uint32_t kLutHi = 0x4180u;                // bf16 bits of 16.0
@@ -804,11 +808,24 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
             oo[k] = (int64_t)row * p.out_stride + col;
         }
     };
+#if RGG_GEGLU_LUT_FIRST
+    // The lane's table vector is fetched before its gate/up vectors: loads
+    // return in order, so the LDS fill and the barrier then overlap the HBM
+    // latency instead of waiting for it.
+    static_assert(kLutEntries / 8 <= kGegluBlock, "one table vector per lane");
+    const uint32_t kt = min(threadIdx.x, kLutEntries / 8 - 1);
+    const v4u tv = reinterpret_cast<const v4u *>(g_gelu_lut)[kt];
+    __builtin_amdgcn_sched_barrier(0);  // keep the table fetch ahead of gate/up
+    fetch(base);  // indexes are clamped, so the first fetch needs no guard
+    if (threadIdx.x < kLutEntries / 8)
+        reinterpret_cast<v4u *>(lut)[threadIdx.x] = tv;
+#else
     if (base < p.vec_total)
         fetch(base);
 
     for (uint32_t k = threadIdx.x; k < kLutEntries / 8; k += kGegluBlock)
         reinterpret_cast<v4u *>(lut)[k] = reinterpret_cast<const v4u *>(g_gelu_lut)[k];
+#endif
     __syncthreads();
 
     while (base < p.vec_total) {
