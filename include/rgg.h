@@ -57,7 +57,7 @@ typedef enum rgg_status {
 } rgg_status;
 
 /*
- * (a1) Hoisted rotary tables.        [ERNIE-fuse §1, _precompute_rope_cos_sin]
+ * (a1) Hoisted rotary tables.                              [ERNIE-fuse §1]
  *
  * The rotary angles `freqs` have the page's shape (S, B, 1, R) in fp32: the
  * angle of sequence position s, batch row b, rotary column j is

@@ -129,7 +129,7 @@ static double keep_exact(double v)
 }
 
 /* ---------------------------------------------------------------------------
- * (a1) hoisted cos/sin tables          [ERNIE-fuse §1, _precompute_rope_cos_sin]
+ * (a1) hoisted cos/sin tables          [ERNIE-fuse §1]
  *
  * freqs has shape (S, B, 1, R): the angle for sequence position s, batch row
  * b, rotary column j is at freqs[s*stride_s + b*stride_b + j].  The page
@@ -199,12 +199,11 @@ ORACLE_API void oracle_rope_angles_grid(int64_t B, int64_t T, int64_t Hg, int64_
 /* ---------------------------------------------------------------------------
  * (a2, a3) rotate-half RoPE with tail passthrough   [ERNIE-fuse §2]
  *
- * The eager chain on the page, for the rotated slice x_rot = x[..., :R]:
- *   x1, x2   = x_rot.chunk(2)               (halves of width h = R/2)
- *   rotated  = cat(-x2, x1)
- *   x_rot    = x_rot * cos + rotated * sin  (two bf16 muls, one bf16 add)
- * followed by concatenating the untouched tail x[..., R:].  With every op
- * rounded to bf16 this is, per column j < R,
+ * The page's eager chain splits the leading R columns into two halves of
+ * width h = R/2, forms the rotate-half partner (the negated second half
+ * followed by the first half), multiplies the columns by cos and the partner
+ * by sin, adds the two products, and appends the untouched columns R..D-1.
+ * With every op rounded to bf16 this is, per column j < R,
  *   out[j] = rnd( rnd(x[j] * c[j]) + rnd(partner[j] * s[j]) ),
  *   partner[j] = -x[j + h] for j < h,  x[j - h] for j >= h,
  * with c, s the full cos/sin row (c[j] and c[j + h] are NOT assumed equal).

@@ -113,18 +113,20 @@ def check_rope_worked_vectors(o):
 
 
 def eager_rope_chain(x_bits, cos_bits, sin_bits):
-    """The page's eager chain, run by PyTorch on the CPU in bf16 [ERNIE-fuse §2]:
-    chunk, neg, cat, mul, mul, add on the rotated slice, then cat the tail."""
+    """The eager bf16 operator chain the page describes [ERNIE-fuse §2], run
+    by PyTorch on the CPU: split the leading R columns into halves, build the
+    rotate-half partner (negated second half, then first half), two bf16
+    products and one bf16 sum, then append the untouched columns."""
     B, S, H, D = x_bits.shape
     R = cos_bits.shape[1]
     x = _torch_bf16(x_bits)
-    cos_ = _torch_bf16(cos_bits).view(B, S, 1, R)
-    sin_ = _torch_bf16(sin_bits).view(B, S, 1, R)
-    x_rot, tail = x[..., :R], x[..., R:]
-    x1, x2 = x_rot.chunk(2, dim=-1)
-    rotated = torch.cat((-x2, x1), dim=-1)
-    x_rot = x_rot * cos_ + rotated * sin_
-    return _bits(torch.cat((x_rot, tail), dim=-1))
+    c = _torch_bf16(cos_bits).view(B, S, 1, R)
+    s = _torch_bf16(sin_bits).view(B, S, 1, R)
+    head, rest = x[..., :R], x[..., R:]
+    lo, hi = head.chunk(2, dim=-1)
+    partner = torch.cat((-hi, lo), dim=-1)
+    turned = head * c + partner * s
+    return _bits(torch.cat((turned, rest), dim=-1))
 
 
 def check_rope_vs_eager_chain(o):
