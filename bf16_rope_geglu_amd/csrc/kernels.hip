@@ -58,6 +58,9 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
 #ifndef RGG_GEGLU_LUT_FIRST
 #define RGG_GEGLU_LUT_FIRST 1    // GEGLU: fetch the lane's GELU-table vector before gate/up
 #endif
+#ifndef RGG_ROPE_TPW_FIT
+#define RGG_ROPE_TPW_FIT 1       // tokens per workgroup: best lane fill of one or two passes
+#endif
 #ifndef RGG_STAGE_FIRST
 #define RGG_STAGE_FIRST 1        // one-token RoPE, R <= 256: fetch the cos/sin row before x
 #endif
@@ -965,6 +968,26 @@ hipError_t launch_build_gelu_table(hipStream_t stream)
 
 int rope_tokens_per_workgroup(int H, int D, int R)
 {
+#if RGG_ROPE_TPW_FIT
+    // Heads small enough that a token's work items fill under one
+    // workgroup pass are grouped: the token count that fills the one or two
+    // passes best (the fewest passes on a tie), with the fp32 cos/sin rows
+    // within 32 KiB of LDS.
+    const int64_t ipt = (int64_t)H * (R / 16 + (D - R) / 8);  // items per token
+    if (ipt <= 0)
+        return 64;
+    int best = 1;
+    double best_fill = 0.0;
+    for (int t = 1; t <= 64 && t * ipt <= 2 * kRopeBlock && t * R * 8 <= 32768; ++t) {
+        const int64_t n = t * ipt, passes = (n + kRopeBlock - 1) / kRopeBlock;
+        const double fill = (double)n / (double)(passes * kRopeBlock);
+        if (fill > best_fill + 1e-9) {
+            best_fill = fill;
+            best = t;
+        }
+    }
+    return best;
+#else
     // About RGG_ROPE_VEC_PER_WG 16-byte vectors of x per workgroup, with the
     // fp32 cos/sin staging within 32 KiB of LDS.
     int64_t vec_per_tok = (int64_t)H * (D / 8);
@@ -976,6 +999,7 @@ int rope_tokens_per_workgroup(int H, int D, int R)
     while (t > 1 && t * R * 8 > 32768)
         --t;
     return (int)t;
+#endif
 }
 
 int geglu_grid(uint32_t vec_total, int cu_count)
