@@ -26,6 +26,13 @@
  *     angle tensor needs 16-byte alignment and strides that are multiples of
  *     4.  There is no slower fallback for other layouts.
  *   - A size of zero in any batch-like dimension is a valid no-op.
+ *   - Index arithmetic in the kernels is 32-bit where it can be: each entry
+ *     point states the size limits beyond which it returns
+ *     RGG_ERR_UNSUPPORTED.
+ *   - Entry points may be called from several host threads at once, on any
+ *     streams; the one-time GELU table build is serialized per device.  Calls
+ *     that write the same memory on different streams race as any kernels
+ *     would.
  */
 #ifndef RGG_H
 #define RGG_H
@@ -72,7 +79,8 @@ typedef enum rgg_status {
  *
  * Requirements: S, B >= 0; R >= 0 and a multiple of 8; freqs 16-byte aligned
  * with stride_s, stride_b multiples of 4; cos_out, sin_out 16-byte aligned;
- * the two tables may not overlap each other or freqs.
+ * the two tables may not overlap each other or freqs.  Limits: S*B < 2^31
+ * and S*B*R/4 < 2^31.
  */
 RGG_API int rope_cossin_precompute(const float *freqs, int64_t S, int64_t B, int64_t R,
                            int64_t stride_s, int64_t stride_b,
@@ -101,6 +109,7 @@ RGG_API int rope_cossin_precompute(const float *freqs, int64_t S, int64_t B, int
  * otherwise); t_offset NULL or a 4-byte aligned device array of B int32;
  * cos_out, sin_out 16-byte aligned device (B*S, R) bf16 tables that overlap
  * neither each other nor t_offset.  Any of B, T, Hg, Wg or R zero: no work.
+ * Limits: S = T*Hg*Wg < 2^31, B*S < 2^31 and B*S*R/16 < 2^31.
  */
 RGG_API int rope_cossin_from_grid(int64_t B, int64_t T, int64_t Hg, int64_t Wg, int32_t d0,
                                   int32_t d1, int32_t d2, double theta, const int32_t *t_offset,
@@ -143,6 +152,9 @@ typedef struct rgg_rope_view {
  * Requirements: B, S, H >= 0; D > 0 and a multiple of 8; R even with
  * 0 <= R <= D and R a multiple of 16 (each half a whole number of 8-element
  * vectors); R = 0 copies x.  Output rows must not overlap each other.
+ * Limits: B*S < 2^31, D <= 8192 and H*D < 2^25 (RGG_ERR_UNSUPPORTED);
+ * longer token ranges than one dispatch takes are split into several
+ * launches on `stream`.
  */
 RGG_API int rope_rotate_half_bf16(const rgg_rope_view *views, int n_views, int64_t B, int64_t S,
                           int64_t H, int64_t D, int64_t R, const uint16_t *cos,
@@ -167,6 +179,7 @@ RGG_API int rope_rotate_half_bf16(const rgg_rope_view *views, int n_views, int64
  *
  * Requirements: rows, hidden >= 0; hidden a multiple of 8; strides multiples
  * of 8 with out_row_stride >= hidden when rows > 1; 16-byte aligned bases.
+ * Limit: rows*hidden/8 < 2^31.
  */
 RGG_API int gelu_and_mul_bf16(const uint16_t *input, int64_t rows, int64_t hidden,
                       int64_t in_row_stride, uint16_t *out, int64_t out_row_stride,

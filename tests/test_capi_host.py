@@ -298,3 +298,17 @@ def test_step_bytes_are_the_three_kernels():
     import bench
 
     assert bench.step_algo_bytes(4) == 33554432 + 1090519040 + 1610612736 == 2734686208
+
+
+def test_size_limits_are_refused_before_any_launch(lib):
+    """Every documented size limit returns RGG_ERR_UNSUPPORTED (the checks run
+    before anything touches a device)."""
+    v = view()
+    assert rope(lib, [v], B=1 << 16, S=1 << 15) == UNSUPPORTED          # B*S = 2^31
+    assert rope(lib, [v], D=8200, R=128) == UNSUPPORTED                   # D > 8192
+    assert rope(lib, [v], H=4096, D=8192, R=128) == UNSUPPORTED           # H*D = 2^25
+    assert gelu(lib, rows=1 << 28, hidden=64, is_=128, os_=64) == UNSUPPORTED  # rows*hidden/8
+    assert cossin(lib, S=1 << 16, B=1 << 15) == UNSUPPORTED              # S*B = 2^31
+    assert cossin(lib, S=1 << 14, B=1 << 14, R=32) == UNSUPPORTED        # S*B*R/4 = 2^31
+    assert grid(lib, B=1, T=1 << 11, Hg=1 << 10, Wg=1 << 10) == UNSUPPORTED  # S = 2^31
+    assert grid(lib, B=1 << 12, T=1, Hg=1 << 10, Wg=1 << 9, d=(16, 8, 8)) == UNSUPPORTED
