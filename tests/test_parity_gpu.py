@@ -23,6 +23,7 @@ import torch
 import bf16_rope_geglu_amd as rgg
 import oracle
 import workloads as W
+from _compare import assert_bitexact, assert_ulp_bar, ordered, say  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
@@ -42,10 +43,6 @@ def orc():
     return oracle.get()
 
 
-def say(*a):
-    print(*a, flush=True)
-
-
 def dev(a):
     a = np.ascontiguousarray(a, dtype=np.uint16)
     return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
@@ -54,30 +51,6 @@ def dev(a):
 def host(t):
     torch.cuda.synchronize()
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-
-def ordered(bits):
-    b = np.asarray(bits, np.int64)
-    return np.where(b & 0x8000, -(b & 0x7FFF), b)
-
-
-def assert_bitexact(got, want, what):
-    got, want = np.asarray(got), np.asarray(want)
-    bad = np.count_nonzero(got != want)
-    say(f"{what}: {got.size} elements, {bad} not bit-identical")
-    if bad:
-        idx = np.argwhere(got != want)[:5]
-        raise AssertionError(f"{what}: {bad} mismatches, first at {idx.tolist()}: "
-                             f"{[hex(int(got[tuple(i)])) for i in idx]} vs "
-                             f"{[hex(int(want[tuple(i)])) for i in idx]}")
-
-
-def assert_ulp_bar(got, want, what):
-    d = np.abs(ordered(got) - ordered(want))
-    bad = np.count_nonzero(got != want)
-    say(f"{what}: {got.size} elements, {bad} not bit-identical, max {int(d.max(initial=0))} ulp")
-    assert d.max(initial=0) <= 1, f"{what}: max ulp {d.max()}"
-    assert bad <= 1e-4 * got.size, f"{what}: {bad} of {got.size} not bit-identical"
 
 
 def with_guards(shape, fill=0x7FC1):
