@@ -132,10 +132,10 @@ typedef struct rgg_rope_view {
 /*
  * (a2, a3) Rotate-half RoPE with tail passthrough.          [ERNIE-fuse §2]
  *
- * For every view v, token (b, s), head h, with c and s the bf16 rows b*S + s
- * of `cos` and `sin` (contiguous (B*S, R)) and h2 = R/2:
- *   j <  h2:      out[j] = rne(rne(x[j]*c[j]) + rne(-x[j+h2]*s[j]))
- *   h2 <= j < R:  out[j] = rne(rne(x[j]*c[j]) + rne( x[j-h2]*s[j]))
+ * For every view v, token (b, s), head h, with c and sn the bf16 rows
+ * b*S + s of `cos` and `sin` (contiguous (B*S, R)) and h2 = R/2:
+ *   j <  h2:      out[j] = rne(rne(x[j]*c[j]) + rne(-x[j+h2]*sn[j]))
+ *   h2 <= j < R:  out[j] = rne(rne(x[j]*c[j]) + rne( x[j-h2]*sn[j]))
  *   R <= j < D:   out[j] = x[j]                       (bits copied)
  * i.e. exactly the eager bf16 chunk / neg / cat / mul / mul / add chain
  * followed by the tail concatenation, every op rounded to nearest-even bf16.
