@@ -43,6 +43,10 @@ class Oracle:
         lib.oracle_rope_angles_grid.argtypes = [_i64, _i64, _i64, _i64,
                                                 ctypes.POINTER(ctypes.c_int32), ctypes.c_double,
                                                 ctypes.POINTER(ctypes.c_int32), _f32p]
+        lib.oracle_gemm_bf16.restype = None
+        lib.oracle_gemm_bf16.argtypes = [_u16p, _i64, _i64, _i64, _u16p, _i64, _i64, _u16p, _i64]
+        lib.oracle_gemm_geglu.restype = ctypes.c_int
+        lib.oracle_gemm_geglu.argtypes = [_u16p, _i64, _i64, _i64, _u16p, _i64, _i64, _u16p, _i64]
         lib.oracle_rope_rows.argtypes = [_u16p, _u16p, _u16p, _i64, _i64, _i64, _u16p]
         lib.oracle_rope_rows.restype = ctypes.c_int
         lib.oracle_rope_rotate_half.argtypes = [_u16p, _i64, _i64, _i64, _i64, _i64,
@@ -115,6 +119,30 @@ class Oracle:
     def rope_cossin_grid(self, B, grid, dims, theta, t_offset=None):
         """The (B*S, R) cos/sin tables of the grid's angles."""
         return self.rope_cossin(self.rope_angles_grid(B, grid, dims, theta, t_offset))
+
+    # -- (f3) gate_up projection and GEGLU on it -----------------------------
+    def gemm_bf16(self, x, w):
+        """x: uint16 (M, K), w: uint16 (N, K).  Returns rne_bf16(x w^T), (M, N)."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.uint16)
+        (M, K), (N, K2) = x.shape, w.shape
+        assert K == K2
+        out = np.empty((M, N), np.uint16)
+        self.lib.oracle_gemm_bf16(_ptr(x, _u16p), M, K, K, _ptr(w, _u16p), N, K,
+                                  _ptr(out, _u16p), N)
+        return out
+
+    def gemm_geglu(self, x, w):
+        """x: uint16 (M, K), w: uint16 (2H, K), gate rows first.  Returns (M, H)."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        w = np.ascontiguousarray(w, dtype=np.uint16)
+        (M, K), (N, K2) = x.shape, w.shape
+        assert K == K2 and N % 2 == 0
+        out = np.empty((M, N // 2), np.uint16)
+        rc = self.lib.oracle_gemm_geglu(_ptr(x, _u16p), M, K, K, _ptr(w, _u16p), N // 2, K,
+                                        _ptr(out, _u16p), N // 2)
+        assert rc == 0
+        return out
 
     # -- (a2, a3) rotate-half ------------------------------------------------
     def rope_rotate_half(self, x, cos, sin):

@@ -369,3 +369,67 @@ ORACLE_API void oracle_gelu_and_mul(const uint16_t *input, int64_t rows, int64_t
         }
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * (f3) the gate_up projection feeding GEGLU, and GEGLU on its output
+ *                                   [ERNIE-fuse §3, the projection before it]
+ *
+ * The page's GEGLU input is the output of the FFN's gate_up linear layer,
+ * computed eagerly as a bf16 matrix product: every product of two bf16
+ * values is accumulated in higher precision and the sum is rounded once to
+ * bf16.  Reading used here (the page shows no bias term): out = x W^T with
+ * x (M, K) and W (N, K), both bf16 row-major with the given row strides,
+ *   out[m][n] = rne_bf16( sum_k x[m][k] * w[n][k] ),
+ * the sum taken exactly.  Each product of two bf16 values is exact in
+ * double; the sum is kept as an unevaluated pair (s, c) updated with the
+ * error-free TwoSum of Knuth, so that s + c carries the sum to about 106
+ * bits, and it is rounded once with the sign of what the final double
+ * addition dropped as the sticky bit.
+ * ------------------------------------------------------------------------- */
+static void two_sum(double a, double b, double *s, double *e)
+{
+    double t = a + b;
+    double bb = t - a;
+    *e = (a - (t - bb)) + (b - bb);
+    *s = t;
+}
+
+ORACLE_API void oracle_gemm_bf16(const uint16_t *x, int64_t M, int64_t K, int64_t x_stride,
+                                 const uint16_t *w, int64_t N, int64_t w_stride, uint16_t *out,
+                                 int64_t out_stride)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0, c = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double prod = oracle_bf16_to_double(x[m * x_stride + k]) *
+                              oracle_bf16_to_double(w[n * w_stride + k]);
+                double e;
+                two_sum(s, prod, &s, &e);
+                c += e;
+            }
+            double hi, lo;
+            two_sum(s, c, &hi, &lo);
+            out[m * out_stride + n] = oracle_double_to_bf16(hi, (lo > 0) - (lo < 0));
+        }
+    }
+}
+
+/*
+ * GEGLU fused after the projection: W holds the gate rows 0 .. H-1 and the
+ * up rows H .. 2H-1, so gate_up = rne_bf16(x W^T) is (M, 2H) with the gate
+ * first, and out = oracle_gelu_and_mul(gate_up), (M, H).
+ */
+ORACLE_API int oracle_gemm_geglu(const uint16_t *x, int64_t M, int64_t K, int64_t x_stride,
+                                 const uint16_t *w, int64_t H, int64_t w_stride, uint16_t *out,
+                                 int64_t out_stride)
+{
+    uint16_t *gate_up = (uint16_t *)malloc((size_t)(M > 0 ? M : 1) * (size_t)(2 * H > 0 ? 2 * H : 1) *
+                                           sizeof(uint16_t));
+    if (!gate_up)
+        return -1;
+    oracle_gemm_bf16(x, M, K, x_stride, w, 2 * H, w_stride, gate_up, 2 * H);
+    oracle_gelu_and_mul(gate_up, M, H, 2 * H, out, out_stride);
+    free(gate_up);
+    return 0;
+}

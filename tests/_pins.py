@@ -392,6 +392,82 @@ def check_mul_rounding_vs_torch(o):
     assert _same_bits_or_both_nan(got, want).all()
 
 
+# ---------------------------------------------------------------------------
+# (f3) the gate_up projection and GEGLU on it
+# ---------------------------------------------------------------------------
+
+def _finite_bits(a):
+    a = np.asarray(a, np.uint16).copy()
+    a[(a & 0x7F80) == 0x7F80] = 0x3F80            # no Inf/NaN operands
+    return a
+
+
+def check_gemm_vs_exact_rationals(o):
+    """Every output is the round-to-nearest-even bf16 of the exact sum of
+    products, computed with Python fractions (exact for binary floats) and
+    judged by distances to the neighbouring bf16 values."""
+    from fractions import Fraction
+    mpmath.mp.prec = 4000
+    for M, K, N, seed, gen in ((3, 1, 4, 11, "normal"), (4, 37, 5, 12, "normal"),
+                               (3, 64, 3, 13, "special"), (2, 130, 4, 14, "special")):
+        g = workloads.special_bf16 if gen == "special" else workloads.normal_bf16
+        x = _finite_bits(g((M, K), 7000 + seed))
+        w = _finite_bits(g((N, K), 7100 + seed))
+        got = o.gemm_bf16(x, w)
+        xv = [[Fraction(bits_to_float(b)) for b in row] for row in x]
+        wv = [[Fraction(bits_to_float(b)) for b in row] for row in w]
+        for m in range(M):
+            for n in range(N):
+                exact = sum((a * b for a, b in zip(xv[m], wv[n])), Fraction(0))
+                v = mpmath.mpf(exact.numerator) / mpmath.mpf(exact.denominator)
+                if abs(v) >= mpmath.mpf(bits_to_float(0x7F7F)) * (1 + mpmath.mpf(2) ** -8):
+                    assert (int(got[m, n]) & 0x7FFF) == 0x7F80, "overflow must give inf"
+                    continue
+                assert is_nearest_bf16(v, int(got[m, n])), (M, K, N, m, n, hex(int(got[m, n])))
+    mpmath.mp.prec = 53
+
+
+def check_gemm_cancellation_ties_and_sticky(o):
+    """Sums that a short accumulator gets wrong: cancellation of huge terms,
+    an exact tie (to even), and a tie broken by a term 2^-60 below it."""
+    def bf(vals):
+        return workloads.f32_to_bf16_bits(np.array(vals, np.float32))
+    cases = [
+        ([2.0 ** 60, 1.0, -2.0 ** 60], 0x3F80),              # exactly 1
+        ([2.0 ** 100, 2.0 ** -100, -2.0 ** 100], int(bf([2.0 ** -100])[0])),
+        ([1.0, 2.0 ** -8], 0x3F80),                           # tie -> even (1.0)
+        ([1.0 + 2.0 ** -7, 2.0 ** -8], 0x3F82),               # tie -> even (0x3F82)
+        ([1.0, 2.0 ** -8, 2.0 ** -60], 0x3F81),               # just above the tie
+        ([1.0, 2.0 ** -8, -2.0 ** -60], 0x3F80),              # just below it
+    ]
+    for vals, want in cases:
+        x = bf(vals).reshape(1, -1)
+        w = bf([1.0] * len(vals)).reshape(1, -1)
+        got = int(o.gemm_bf16(x, w)[0, 0])
+        assert got == want, (vals, hex(got), hex(want))
+
+
+def check_gemm_geglu_vs_eager(o):
+    """GEGLU on the projection against PyTorch's CPU eager chain: a float32
+    matmul of small integers (exact), the bf16 cast of the projection, then
+    up * gelu(gate) in bf16, bit for bit where float GELU is exact
+    (gates in [-3, 2^60])."""
+    rng = np.random.Generator(np.random.PCG64(8101))
+    M, K, H = 6, 24, 10
+    xf = rng.integers(-3, 4, size=(M, K)).astype(np.float32) * 0.25
+    wf = rng.integers(-3, 4, size=(2 * H, K)).astype(np.float32) * 0.125
+    x = workloads.f32_to_bf16_bits(xf)
+    w = workloads.f32_to_bf16_bits(wf)
+    got = o.gemm_geglu(x, w)
+    gate_up = (torch.from_numpy(xf) @ torch.from_numpy(wf).T).to(torch.bfloat16)
+    gate, up = gate_up[:, :H], gate_up[:, H:]
+    want = _bits(up * torch.nn.functional.gelu(gate))
+    g = gate.float().numpy()
+    ok = (g >= -3.0)
+    assert ok.mean() > 0.9
+    assert np.array_equal(got[ok], want[ok]), (got[ok], want[ok])
+
+
 def _ordered(bits):
     b = np.asarray(bits, np.int64)
     return np.where(b & 0x8000, -(b & 0x7FFF), b)
@@ -413,4 +489,7 @@ ALL_CHECKS = [
     check_gelu_and_mul_vs_eager,
     check_mul_rounding_vs_torch,
     check_gelu_exhaustive_mpmath,
+    check_gemm_vs_exact_rationals,
+    check_gemm_cancellation_ties_and_sticky,
+    check_gemm_geglu_vs_eager,
 ]

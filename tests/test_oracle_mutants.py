@@ -51,6 +51,15 @@ MUTANTS = {
     "grid_offset_ignored": (
         "(double)(t + (t_offset ? t_offset[b] : 0))",
         "(double)t"),
+    "gemm_uncompensated_sum": (
+        "                c += e;",
+        "                c += 0.0 * e;"),
+    "gemm_sticky_ignored": (
+        "out[m * out_stride + n] = oracle_double_to_bf16(hi, (lo > 0) - (lo < 0));",
+        "out[m * out_stride + n] = oracle_double_to_bf16(hi, 0);"),
+    "gemm_last_term_dropped": (
+        "for (int64_t k = 0; k < K; ++k) {\n                double prod",
+        "for (int64_t k = 0; k < K - 1; ++k) {\n                double prod"),
     "gelu_without_sqrt2": (
         "return 0.5 * x * erfc(-x / sqrt(2.0));",
         "return 0.5 * x * erfc(-x);"),
