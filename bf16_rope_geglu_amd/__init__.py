@@ -12,9 +12,12 @@ Method: "[sglang] ERNIE-Image의 RoPE와 GELU-mul 융합 및 RoPE cos/sin 호이
                              positions (a reading of the angle producer)
   rope_rotate_half_bf16   -- §2, bit-exact rotate-half RoPE, tail passthrough
   gelu_and_mul_bf16       -- §3, GEGLU with bf16 activation rounding
+  gemm_bf16_nt,           -- §3, the gate_up projection before GEGLU, alone
+  gemm_geglu_bf16            or with GEGLU in its epilogue (on the matrix cores)
 The page's own Python names are kept as aliases at the bottom.
 """
 import ctypes
+import math
 import os
 
 import torch  # must come first: the HIP runtime torch has loaded is the one librgg binds to
@@ -24,7 +27,7 @@ LIBRARY = os.path.join(_HERE, "lib", "librgg.so")
 
 __all__ = [
     "rope_cossin_precompute", "rope_cossin_from_grid", "rope_rotate_half_bf16",
-    "gelu_and_mul_bf16", "prepare_device", "selfcheck", "RggError", "library",
+    "gelu_and_mul_bf16", "gemm_bf16_nt", "gemm_geglu_bf16", "prepare_device", "selfcheck", "RggError", "library",
     "precompute_rope_cos_sin", "fused_rope_rotate_half_bitexact",
     "gelu_and_mul_with_activation_rounding",
 ]
@@ -65,12 +68,15 @@ def library():
         lib.rope_rotate_half_bf16.argtypes = [ctypes.POINTER(RopeView), ctypes.c_int, _I, _I, _I,
                                               _I, _I, _P, _P, _P]
         lib.gelu_and_mul_bf16.argtypes = [_P, _I, _I, _I, _P, _I, _P]
+        lib.gemm_bf16_nt.argtypes = [_P, _I, _I, _I, _P, _I, _I, _P, _I, _P]
+        lib.gemm_geglu_bf16.argtypes = [_P, _I, _I, _I, _P, _I, _I, _P, _I, _P]
         lib.rgg_prepare_device.argtypes = [ctypes.c_int]
         lib.rgg_selfcheck.argtypes = [_P, _I, _P, ctypes.POINTER(ctypes.c_uint32)]
         lib.rgg_status_string.argtypes = [ctypes.c_int]
         lib.rgg_status_string.restype = ctypes.c_char_p
         for f in (lib.rope_cossin_precompute, lib.rope_cossin_from_grid,
-                  lib.rope_rotate_half_bf16, lib.gelu_and_mul_bf16, lib.rgg_prepare_device,
+                  lib.rope_rotate_half_bf16, lib.gelu_and_mul_bf16, lib.gemm_bf16_nt,
+                  lib.gemm_geglu_bf16, lib.rgg_prepare_device,
                   lib.rgg_selfcheck):
             f.restype = ctypes.c_int
         _lib = lib
@@ -245,6 +251,64 @@ def gelu_and_mul_bf16(input, out=None):
             inp2.data_ptr(), rows, hidden, inp2.stride(0) if rows else 2 * hidden,
             out2.data_ptr(), out2.stride(0) if rows else hidden, _stream(dev)))
     return out
+
+
+def _projection(name, x, weight, out_cols, out):
+    """Shared marshalling of gemm_bf16_nt / gemm_geglu_bf16: x (..., K) rows,
+    weight (N, K); returns out (..., out_cols).  The size argument of the C
+    call is out_cols for both (N for the plain product, hidden for GEGLU)."""
+    _need(x, torch.bfloat16, "x")
+    _need(weight, torch.bfloat16, "weight")
+    if x.dim() < 1 or weight.dim() != 2 or weight.shape[1] != x.shape[-1]:
+        raise ValueError("x must be (..., K) and weight (N, K)")
+    K = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    if out is None:
+        out = torch.empty(lead + (out_cols,), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out")
+    if tuple(out.shape) != lead + (out_cols,):
+        raise ValueError(f"out must have shape (..., {out_cols})")
+    M = math.prod(lead)
+    xp, xs = 0, K
+    if M and K:
+        x2 = x.reshape(M, K)
+        if x2.data_ptr() != x.data_ptr() or x2.stride(1) != 1:
+            raise ValueError("x's leading dimensions must collapse into rows without a copy")
+        xp, xs = x2.data_ptr(), (x2.stride(0) if M > 1 else K)
+    if weight.numel() and weight.stride(1) != 1:
+        raise ValueError("weight needs unit stride along K")
+    op, os_ = 0, out_cols
+    if M and out_cols:
+        out2 = out.view(M, out_cols)
+        if out2.stride(1) != 1:
+            raise ValueError("out needs unit stride along its last dimension")
+        op, os_ = out2.data_ptr(), (out2.stride(0) if M > 1 else out_cols)
+    dev = x.device
+    _one_device(dev, weight=weight, out=out)
+    with torch.cuda.device(dev):
+        _check(name, getattr(library(), name)(
+            xp, M, K, xs, weight.data_ptr() if weight.numel() else 0, out_cols,
+            weight.stride(0) if weight.shape[0] > 1 and K else K, op, os_, _stream(dev)))
+    return out
+
+
+def gemm_bf16_nt(x, weight, out=None):
+    """The gate_up projection: x (..., K) bf16 times weight (N, K) bf16
+    transposed (a linear layer without bias), fp32 accumulation, each output
+    rounded once to bf16; returns (..., N).  K a multiple of 64, N of 128."""
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 2:
+        raise ValueError("weight must be (N, K)")
+    return _projection("gemm_bf16_nt", x, weight, weight.shape[0], out)
+
+
+def gemm_geglu_bf16(x, weight, out=None):
+    """GEGLU fused into the gate_up projection: weight (2*hidden, K) holds the
+    gate rows then the up rows; returns rne_bf16(up * rne_bf16(gelu(gate))) of
+    shape (..., hidden), bit for bit gelu_and_mul_bf16(gemm_bf16_nt(x, weight))
+    without the (..., 2*hidden) projection in memory."""
+    if not isinstance(weight, torch.Tensor) or weight.dim() != 2 or weight.shape[0] % 2:
+        raise ValueError("weight must be (2*hidden, K)")
+    return _projection("gemm_geglu_bf16", x, weight, weight.shape[0] // 2, out)
 
 
 def prepare_device(device=None):

@@ -308,6 +308,87 @@ int rope_rotate_half_bf16(const rgg_rope_view *views, int n_views, int64_t B, in
     return rgg::launch_rope_rotate_half(p, stream) == hipSuccess ? RGG_OK : RGG_ERR_HIP;
 }
 
+namespace {
+
+// Shared checks of the two projection entry points; `H` is half the
+// projection width (the gate/up split), `out_cols` the output row width.
+int gemm_checks(const uint16_t *x, int64_t M, int64_t K, int64_t x_stride, const uint16_t *w,
+                int64_t H, int64_t w_stride, const uint16_t *out, int64_t out_cols,
+                int64_t out_stride, rgg::GemmParams &p)
+{
+    if (M < 0 || K < 0 || H < 0 || x_stride < 0 || w_stride < 0 || out_stride < 0)
+        return RGG_ERR_SHAPE;
+    if (K % 64 != 0 || H % 64 != 0)
+        return RGG_ERR_UNSUPPORTED;
+    if ((M > 1 && x_stride < K) || (H > 0 && w_stride < K) || (M > 1 && out_stride < out_cols))
+        return RGG_ERR_UNSUPPORTED;
+    if (M == 0 || H == 0)
+        return -1;  // nothing to do
+    if (!out || (K > 0 && (!x || !w)))
+        return RGG_ERR_NULL;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(out) || x_stride % 8 || w_stride % 8 ||
+        out_stride % 8)
+        return RGG_ERR_ALIGN;
+    const int64_t mblocks = (M + 127) / 128, nblocks = H / 64;
+    if (M >= kMax32 || mblocks * nblocks >= ((int64_t)1 << 24) || H >= kMax32 / 2)
+        return RGG_ERR_UNSUPPORTED;
+    if (K > 0) {
+        const int64_t xn[1] = {M}, xs[1] = {x_stride}, wn[1] = {2 * H}, ws[1] = {w_stride};
+        const int64_t on[1] = {M}, os[1] = {out_stride};
+        Layout lx = make_layout(x, 2, 1, xn, xs, K);
+        Layout lw = make_layout(w, 2, 1, wn, ws, K);
+        Layout lo = make_layout(out, 2, 1, on, os, out_cols);
+        if (may_overlap(lo, lx) || may_overlap(lo, lw))
+            return RGG_ERR_ALIAS;
+    }
+    memset(&p, 0, sizeof p);
+    p.x = x;
+    p.w = w;
+    p.out = const_cast<uint16_t *>(out);
+    p.x_stride = x_stride;
+    p.w_stride = w_stride;
+    p.out_stride = out_stride;
+    p.M = M;
+    p.H = (int32_t)H;
+    p.k_tiles = (int32_t)(K / 64);
+    p.div_nblocks = make_fastdiv((uint32_t)nblocks);
+    return RGG_OK;
+}
+
+}  // namespace
+
+int gemm_bf16_nt(const uint16_t *x, int64_t M, int64_t K, int64_t x_stride, const uint16_t *w,
+                 int64_t N, int64_t w_stride, uint16_t *out, int64_t out_stride,
+                 hipStream_t stream)
+{
+    if (N < 0)
+        return RGG_ERR_SHAPE;
+    if (N % 128 != 0)
+        return RGG_ERR_UNSUPPORTED;
+    rgg::GemmParams p;
+    int st = gemm_checks(x, M, K, x_stride, w, N / 2, w_stride, out, N, out_stride, p);
+    if (st != RGG_OK)
+        return st < 0 ? RGG_OK : st;
+    return rgg::launch_gemm_gate_up(p, false, stream) == hipSuccess ? RGG_OK : RGG_ERR_HIP;
+}
+
+int gemm_geglu_bf16(const uint16_t *x, int64_t M, int64_t K, int64_t x_stride, const uint16_t *w,
+                    int64_t H, int64_t w_stride, uint16_t *out, int64_t out_stride,
+                    hipStream_t stream)
+{
+    rgg::GemmParams p;
+    int st = gemm_checks(x, M, K, x_stride, w, H, w_stride, out, H, out_stride, p);
+    if (st != RGG_OK)
+        return st < 0 ? RGG_OK : st;
+    int dev;
+    if (current_device(dev) != RGG_OK)
+        return RGG_ERR_HIP;
+    st = ensure_table(dev, stream);
+    if (st != RGG_OK)
+        return st;
+    return rgg::launch_gemm_gate_up(p, true, stream) == hipSuccess ? RGG_OK : RGG_ERR_HIP;
+}
+
 int gelu_and_mul_bf16(const uint16_t *input, int64_t rows, int64_t hidden, int64_t in_row_stride,
                       uint16_t *out, int64_t out_row_stride, hipStream_t stream)
 {

@@ -16,6 +16,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "launch.h"
 
@@ -844,6 +845,141 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
     }
 }
 
+// ---------------------------------------------------------------------------
+// (f3) GEGLU as the epilogue of the gate_up projection      [ERNIE-fuse §3]
+//
+// out = x W^T on the matrix cores (v_mfma_f32_32x32x16_bf16, fp32
+// accumulation), the eager bf16 rounding of the projection applied to each
+// accumulator, then either stored or turned into up * G(gate) in the
+// epilogue, so the (M, 2H) intermediate never goes to memory.
+//
+// A 256-thread workgroup computes 128 rows x 64 output columns: it stages,
+// per 64-wide slice of K, 128 rows of x and the 64 gate rows plus the 64
+// matching up rows of W in LDS (double buffered, rows padded to 72 elements
+// against bank conflicts; the next slice's global loads are in flight while
+// the current one is multiplied).  Wave (wm, wn) owns rows wm*64 .. +63 and
+// columns wn*32 .. +31 of both the gate and the up block, so one lane holds
+// the gate and the up accumulator of the same (row, column): lane l of a
+// 32x32 block holds column l % 32 and, in its 16 accumulators v, rows
+// (v / 4) * 8 + (l / 32) * 4 + v % 4.  Operands: lane l supplies row (of x)
+// or column (row of W) l % 32 and the 8 consecutive k at (l / 32) * 8.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kGemmBM = 128;              // rows of x per workgroup
+constexpr int kGemmBN = 64;               // gate (and up) columns per workgroup
+constexpr int kGemmBK = 64;               // K slice per stage
+constexpr int kGemmLd = kGemmBK + 8;      // padded LDS row, elements
+constexpr int kGemmTile = 128 * kGemmLd;  // one staged operand, elements
+constexpr size_t kGemmLds = 2 * 2 * kGemmTile * sizeof(uint16_t);
+
+__device__ __forceinline__ uint32_t bf16_of(float v) { return rne_pack(v, 0.0f) & 0xFFFFu; }
+
+template <bool Geglu>
+__global__ __launch_bounds__(256) void gemm_gate_up_kernel(GemmParams p)
+{
+    extern __shared__ __align__(16) uint16_t gsm[];  // [stage][x | W][128][kGemmLd]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t mb = fdiv(blockIdx.x, p.div_nblocks);
+    const uint32_t nb = blockIdx.x - mb * p.div_nblocks.d;
+    const int64_t m0 = (int64_t)mb * kGemmBM, n0 = (int64_t)nb * kGemmBN;
+
+    // Each thread moves 4 + 4 16-byte vectors per K slice: vector v = tid +
+    // 256 i is row v / 8, k vector v % 8 of the staged x rows and W rows.
+    // Rows past M re-read row M-1 (their results are not stored).
+    const uint16_t *gx[4], *gw[4];
+    int so[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int v = tid + 256 * i, row = v >> 3, kv = v & 7;
+        const int64_t m = min(m0 + row, p.M - 1);
+        const int64_t wr = row < kGemmBN ? n0 + row : (int64_t)p.H + n0 + (row - kGemmBN);
+        gx[i] = p.x + m * p.x_stride + kv * 8;
+        gw[i] = p.w + wr * p.w_stride + kv * 8;
+        so[i] = row * kGemmLd + kv * 8;
+    }
+    v4u rx[4], rw[4];
+    auto fetch = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            rx[i] = *reinterpret_cast<const v4u *>(gx[i] + (int64_t)kt * kGemmBK);
+            rw[i] = *reinterpret_cast<const v4u *>(gw[i] + (int64_t)kt * kGemmBK);
+        }
+    };
+    auto stage = [&](int buf) {
+        uint16_t *sx = gsm + buf * 2 * kGemmTile, *sw = sx + kGemmTile;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<v4u *>(sx + so[i]) = rx[i];
+            *reinterpret_cast<v4u *>(sw + so[i]) = rw[i];
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[a][b][v] = 0.0f;
+
+    const int KT = p.k_tiles;
+    if (KT > 0) {
+        fetch(0);
+        stage(0);
+    }
+    __syncthreads();
+    const int ra = wm * 64 + (lane & 31);           // x row (of the tile) for row block 0
+    const int rg = wn * 32 + (lane & 31);           // W row (of the tile) of the gate column
+    const int kl = (lane >> 5) * 8;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT)
+            fetch(kt + 1);
+        const uint16_t *sx = gsm + buf * 2 * kGemmTile, *sw = sx + kGemmTile;
+#pragma unroll
+        for (int ks = 0; ks < kGemmBK / 16; ++ks) {
+            const int k = ks * 16 + kl;
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(sx + ra * kGemmLd + k);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(sx + (ra + 32) * kGemmLd + k);
+            const bf16x8 bg = *reinterpret_cast<const bf16x8 *>(sw + rg * kGemmLd + k);
+            const bf16x8 bu = *reinterpret_cast<const bf16x8 *>(sw + (rg + kGemmBN) * kGemmLd + k);
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bg, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bu, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bg, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bu, acc[1][1], 0, 0, 0);
+        }
+        if (kt + 1 < KT)
+            stage(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: round each accumulator to bf16 (the projection's output),
+    // then store it, or store rne(up * G(gate)).
+    const int64_t col = n0 + wn * 32 + (lane & 31);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t row = m0 + wm * 64 + rb * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+            if (row >= p.M)
+                continue;
+            const uint32_t g = bf16_of(acc[rb][0][v]), u = bf16_of(acc[rb][1][v]);
+            uint16_t *o = p.out + row * p.out_stride;
+            if (Geglu) {
+                const uint32_t G = gelu_general(g, g_gelu_lut);
+                o[col] = (uint16_t)bf16_of(bf_lo(u) * bf_lo(G));
+            } else {
+                o[col] = (uint16_t)g;
+                o[col + p.H] = (uint16_t)u;
+            }
+        }
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -956,6 +1092,30 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
 hipError_t launch_gelu_and_mul(const GegluParams &p, int grid, hipStream_t stream)
 {
     hipLaunchKernelGGL(gelu_and_mul_kernel, dim3(grid), dim3(kGegluBlock), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_gate_up(const GemmParams &p, bool geglu, hipStream_t stream)
+{
+    // The double-buffered tiles take 72 KiB of LDS, above the 64 KiB a launch
+    // gets without asking; the attribute is per kernel and process-wide.
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_gate_up_kernel<true>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+        if (attr == hipSuccess)
+            attr = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_gate_up_kernel<false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+    });
+    if (attr != hipSuccess)
+        return attr;
+    const uint32_t mblocks = (uint32_t)((p.M + kGemmBM - 1) / kGemmBM);
+    const dim3 grid(mblocks * p.div_nblocks.d), block(256);
+    if (geglu)
+        hipLaunchKernelGGL(gemm_gate_up_kernel<true>, grid, block, kGemmLds, stream, p);
+    else
+        hipLaunchKernelGGL(gemm_gate_up_kernel<false>, grid, block, kGemmLds, stream, p);
     return hipGetLastError();
 }
 

@@ -98,11 +98,26 @@ struct GegluParams {
     FastDiv div_vecs;      // divisor hidden / 8: vector -> (row, column group)
 };
 
+// The gate_up projection x W^T (bf16, fp32 accumulation) with its output
+// rounded to bf16, either stored (gate columns 0..H-1, up columns H..2H-1)
+// or passed through GEGLU in the epilogue.
+struct GemmParams {
+    const uint16_t *x;     // (M, K), row stride x_stride
+    const uint16_t *w;     // (2H, K), row stride w_stride: gate rows, then up rows
+    uint16_t *out;         // (M, 2H) or, with GEGLU, (M, H); row stride out_stride
+    int64_t x_stride, w_stride, out_stride;
+    int64_t M;
+    int32_t H;
+    int32_t k_tiles;       // K / 64
+    FastDiv div_nblocks;   // divisor H / 64: workgroup -> (row block, column block)
+};
+
 // Launchers: enqueue on `stream`, return the hipError_t of the launch.
 hipError_t launch_rope_cossin(const CosSinParams &p, hipStream_t stream);
 hipError_t launch_rope_cossin_grid(const CosSinGridParams &p, hipStream_t stream);
 hipError_t launch_rope_rotate_half(const RopeParams &p, hipStream_t stream);
 hipError_t launch_gelu_and_mul(const GegluParams &p, int grid, hipStream_t stream);
+hipError_t launch_gemm_gate_up(const GemmParams &p, bool geglu, hipStream_t stream);
 hipError_t launch_build_gelu_table(hipStream_t stream);
 
 // Tunables chosen by the host layer.

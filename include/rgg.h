@@ -186,6 +186,41 @@ RGG_API int gelu_and_mul_bf16(const uint16_t *input, int64_t rows, int64_t hidde
                       hipStream_t stream);
 
 /*
+ * (f3) The gate_up projection, alone or with GEGLU fused into its epilogue.
+ *                                   [ERNIE-fuse §3, the projection before it]
+ *
+ * x is (M, K) bf16 with row stride x_stride; W is a linear layer's weight
+ * (N, K) bf16 with row stride w_stride (row n produces output column n).
+ * The product runs on the matrix cores with fp32 accumulation and each
+ * result is rounded once to bf16 (the eager bf16 projection, no bias):
+ *     gemm_bf16_nt:     out[m][n] = rne_bf16( sum_k x[m][k] * W[n][k] ),
+ *                       out (M, N), row stride out_stride.
+ *     gemm_geglu_bf16:  W is (2H, K), gate rows 0..H-1 then up rows H..2H-1;
+ *                       out[m][j] = rne_bf16( up[m][j] * G(gate[m][j]) ) with
+ *                       gate/up the bf16 projection outputs and G as in
+ *                       gelu_and_mul_bf16; out (M, H), row stride out_stride.
+ *                       The (M, 2H) projection never goes to memory.
+ * For the same x and W, gemm_geglu_bf16 returns bit for bit what
+ * gelu_and_mul_bf16 returns on the output of gemm_bf16_nt (one accumulation
+ * order serves both).  The fp32 accumulation order is the kernel's, so a
+ * projection output can differ by one bf16 step from the exactly rounded sum
+ * when that sum lies within the accumulation error of a rounding boundary.
+ *
+ * Requirements: M, K >= 0; K a multiple of 64; N a multiple of 128 (H a
+ * multiple of 64); rows of x and W at least K long, output rows at least N
+ * (H) long; 16-byte aligned bases and strides that are multiples of 8; out
+ * may not overlap x or W.  M or N (H) zero: no work; K zero: zeros (and G(0)).
+ * Limits: M < 2^31 and ceil(M/128) * N/128 < 2^24.  gemm_geglu_bf16 builds
+ * the GELU table like gelu_and_mul_bf16 (RGG_ERR_CAPTURING applies).
+ */
+RGG_API int gemm_bf16_nt(const uint16_t *x, int64_t M, int64_t K, int64_t x_stride,
+                         const uint16_t *w, int64_t N, int64_t w_stride, uint16_t *out,
+                         int64_t out_stride, hipStream_t stream);
+RGG_API int gemm_geglu_bf16(const uint16_t *x, int64_t M, int64_t K, int64_t x_stride,
+                            const uint16_t *w, int64_t H, int64_t w_stride, uint16_t *out,
+                            int64_t out_stride, hipStream_t stream);
+
+/*
  * Builds the constant GELU table on HIP device `device` now (synchronously)
  * if it is not built yet.  Needed only before capturing a GEGLU call into a
  * HIP graph on a device that has not run one; otherwise the first

@@ -41,8 +41,9 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) == {"rope_cossin_precompute", "rope_cossin_from_grid",
-                          "rope_rotate_half_bf16", "gelu_and_mul_bf16", "rgg_prepare_device",
-                          "rgg_selfcheck", "rgg_status_string"}
+                          "rope_rotate_half_bf16", "gelu_and_mul_bf16", "gemm_bf16_nt",
+                          "gemm_geglu_bf16", "rgg_prepare_device", "rgg_selfcheck",
+                          "rgg_status_string"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", rgg.LIBRARY], capture_output=True,
@@ -158,6 +159,47 @@ def test_gelu_checks(lib):
     assert gelu(lib, out=A, os_=64) == ALIAS          # in place needs the input's row stride
     assert gelu(lib, rows=0) == OK
     assert gelu(lib, hidden=0, inp=None) == OK
+
+
+def gemm(lib, x=A, M=256, K=128, xs=128, w=A + (1 << 24), N=256, ws=128, out=A + (1 << 25),
+         os_=256, geglu=False):
+    f = lib.gemm_geglu_bf16 if geglu else lib.gemm_bf16_nt
+    return f(x, M, K, xs, w, N, ws, out, os_, None)
+
+
+@pytest.mark.parametrize("geglu", [False, True])
+def test_gemm_checks(lib, geglu):
+    N = 128 if geglu else 256          # hidden for the fused form, 2*hidden for the plain one
+    g = lambda **kw: gemm(lib, N=kw.pop("N", N), os_=kw.pop("os_", N), geglu=geglu, **kw)
+    assert g(M=-1) == SHAPE
+    assert g(K=-64) == SHAPE
+    assert g(N=-128) == SHAPE
+    assert g(xs=-128) == SHAPE
+    assert g(K=96, xs=96, ws=96) == UNSUPPORTED        # K not a multiple of 64
+    assert g(N=N + 32, os_=N + 32) == UNSUPPORTED      # hidden not a multiple of 64
+    assert g(xs=64) == UNSUPPORTED                     # x rows shorter than K
+    assert g(ws=64) == UNSUPPORTED                     # W rows shorter than K
+    assert g(os_=N - 8) == UNSUPPORTED                 # output rows shorter than the output
+    assert g(x=None) == NULL
+    assert g(w=None) == NULL
+    assert g(out=None) == NULL
+    assert g(x=A + 8) == ALIGN
+    assert g(w=A + (1 << 24) + 2) == ALIGN
+    assert g(xs=136 + 4) == ALIGN
+    assert g(os_=N + 4) == ALIGN
+    assert g(out=A + 4096) == ALIAS                    # inside x
+    assert g(out=A + (1 << 24) + 4096) == ALIAS        # inside W
+    assert g(M=0) == OK
+    assert g(N=0, os_=0, w=None) == OK
+    assert g(M=1 << 31) == UNSUPPORTED                 # M >= 2^31
+    h = 1 << 13                                        # 2^7 column tiles of 64
+    assert g(M=1 << 24, N=h * (1 if geglu else 2),
+             os_=h * (1 if geglu else 2)) == UNSUPPORTED   # 2^17 x 2^7 = 2^24 tiles
+
+
+def test_gemm_plain_needs_whole_gate_up_pairs(lib):
+    assert gemm(lib, N=192, os_=192) == UNSUPPORTED    # N = 2*96: hidden not a multiple of 64
+    assert gemm(lib, N=-1) == SHAPE
 
 
 def test_prepare_device_bad_index(lib):

@@ -639,6 +639,161 @@ def test_geglu_full_size(orc, wid):
 
 
 # ---------------------------------------------------------------------------
+# (f3) the gate_up projection, alone and with GEGLU in its epilogue
+#
+# Bars: on exact-sum inputs (small integers times 2^-4: every partial sum is
+# exact in fp32, whatever the order) the projection and the fused GEGLU are
+# bit-exact with the oracle.  On Gaussian inputs every projection output must
+# be a bf16 rounding of a value within the fp32 accumulation bound
+# 2 (K + 16) 2^-24 sum_k |x_k w_k| of the exact sum, and at least 99% of
+# outputs must equal the oracle's correctly rounded sum.  The fused form must
+# equal GEGLU of the plain projection bit for bit (one accumulation order).
+# ---------------------------------------------------------------------------
+
+def bf16_rne_f64(v):
+    """Round float64 values to bf16 bits, ties to even (normal range)."""
+    v = np.asarray(v, np.float64)
+    m, e = np.frexp(v)
+    r = np.rint(m * 256.0) * np.ldexp(1.0, e - 8)     # 8 significant bits
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def check_projection_bound(x, w, got, orc_out, what):
+    """got (M, N) bf16 bits of x (M, K) @ w (N, K)^T: each a rounding of a
+    value within the fp32 accumulation bound of the exact sum; >= 99% equal to
+    the oracle's correctly rounded sum."""
+    xf = W.bf16_bits_to_f32(x).astype(np.float64)
+    wf = W.bf16_bits_to_f32(w).astype(np.float64)
+    exact = xf @ wf.T
+    mag = np.abs(xf) @ np.abs(wf).T
+    K = x.shape[1]
+    E = 2.0 * (K + 16) * 2.0 ** -24 * mag + 2.0 ** -40 * mag
+    lo, hi = ordered(bf16_rne_f64(exact - E)), ordered(bf16_rne_f64(exact + E))
+    g = ordered(got)
+    outside = np.count_nonzero((g < lo) | (g > hi))
+    same = np.count_nonzero(got == orc_out)
+    d = np.abs(g - ordered(orc_out))
+    say(f"{what}: {got.size} outputs, {got.size - same} differ from the oracle "
+        f"(max {int(d.max(initial=0))} ulp), {outside} outside the accumulation bound")
+    assert outside == 0, f"{what}: {outside} outputs outside the fp32 accumulation bound"
+    assert same >= 0.99 * got.size, f"{what}: only {same} of {got.size} equal the oracle"
+
+
+def padded(a, cols, fill=0x7FC1):
+    """a (rows, c) bf16 bits inside a (rows, cols) device buffer; returns
+    (buffer, view of a)."""
+    rows, c = a.shape
+    full = np.full((rows, cols), fill, np.uint16)
+    full[:, :c] = a
+    buf = dev(full)
+    return buf, buf[:, :c]
+
+
+GEMM_EXACT = [  # M, K, hidden, x row pad, out row pad
+    (1, 64, 64, 0, 0),
+    (127, 64, 64, 8, 0),
+    (128, 128, 128, 0, 16),
+    (129, 192, 64, 24, 8),
+    (300, 256, 192, 0, 0),
+    (1000, 128, 320, 8, 24),
+    (2053, 512, 128, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", GEMM_EXACT, ids=lambda c: "M{}K{}H{}".format(*c[:3]))
+def test_gemm_exact_sums_bitexact(orc, case):
+    """Exact-sum inputs: the plain projection and the fused GEGLU equal the
+    oracle bit for bit, ragged M included; row padding is left untouched."""
+    M, K, H, xpad, opad = case
+    say(f"gemm exact sums {case}")
+    x = W.small_int_bf16((M, K), 9100 + M)
+    w = W.small_int_bf16((2 * H, K), 9200 + K + H)
+    xb, xd = padded(x, K + xpad)
+    _, wd = padded(w, K)
+    pbuf = torch.full((M, 2 * H + opad), 0x7FC1, dtype=torch.int16,
+                      device="cuda").view(torch.bfloat16)
+    rgg.gemm_bf16_nt(xd, wd, out=pbuf[:, :2 * H])
+    fbuf = torch.full((M, H + opad), 0x7FC1, dtype=torch.int16,
+                      device="cuda").view(torch.bfloat16)
+    rgg.gemm_geglu_bf16(xd, wd, out=fbuf[:, :H])
+    pb, fb = host(pbuf), host(fbuf)
+    assert (pb[:, 2 * H:] == 0x7FC1).all() and (fb[:, H:] == 0x7FC1).all(), "wrote into padding"
+    assert np.array_equal(host(xb)[:, :K], x), "x modified"
+    assert_bitexact(pb[:, :2 * H], orc.gemm_bf16(x, w), f"projection {case}")
+    assert_bitexact(fb[:, :H], orc.gemm_geglu(x, w), f"fused geglu {case}")
+
+
+@pytest.mark.parametrize("case", [(200, 256, 128, 1.0), (515, 1024, 192, 1.0),
+                                  (64, 4096, 64, 3.0)],
+                         ids=["M200K256", "M515K1024", "M64K4096"])
+def test_gemm_gaussian_within_accumulation_bound(orc, case):
+    """Gaussian x and 1/sqrt(K)-scaled weights: the projection within the
+    accumulation bound of the exact sum, the fused form equal to GEGLU of it."""
+    M, K, H, gsig = case
+    say(f"gemm gaussian {case}")
+    x = W.normal_bf16((M, K), 9300 + K)
+    w = W.normal_bf16((2 * H, K), 9400 + K, gsig / np.sqrt(K))
+    xd, wd = dev(x), dev(w)
+    plain = rgg.gemm_bf16_nt(xd, wd)
+    fused = host(rgg.gemm_geglu_bf16(xd, wd))
+    again = host(rgg.gelu_and_mul_bf16(plain))
+    p = host(plain)
+    check_projection_bound(x, w, p, orc.gemm_bf16(x, w), f"projection {case}")
+    assert_bitexact(fused, again, f"fused == gelu_and_mul(projection) {case}")
+    assert_ulp_bar(fused, orc.gelu_and_mul(p), f"fused vs oracle GEGLU of the projection {case}")
+
+
+def test_gemm_zero_k_and_empty(orc):
+    """K = 0: every projection output is +0 and GEGLU of it is +0; M = 0 and
+    hidden = 0 are no-ops."""
+    say("gemm K=0 / empty")
+    x = torch.empty((5, 0), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((128, 0), dtype=torch.bfloat16, device="cuda")
+    p = rgg.gemm_bf16_nt(x, w, out=torch.full((5, 128), 3.0, dtype=torch.bfloat16, device="cuda"))
+    f = rgg.gemm_geglu_bf16(x, w, out=torch.full((5, 64), 3.0, dtype=torch.bfloat16, device="cuda"))
+    assert (host(p) == 0).all() and (host(f) == 0).all()
+    e = rgg.gemm_geglu_bf16(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"),
+                            dev(W.normal_bf16((128, 64), 9501)))
+    assert e.shape == (0, 64)
+    h0 = rgg.gemm_bf16_nt(dev(W.normal_bf16((3, 64), 9502)),
+                          torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"))
+    assert h0.shape == (3, 0)
+
+
+def test_gemm_full_size(orc):
+    """The dit-layer projection at its full size, 32768 x 4096 times
+    (2 x 8192) x 4096: exact-sum inputs bit-exact with the oracle on sampled
+    rows; Gaussian inputs within the accumulation bound on sampled rows; the
+    fused output equal to GEGLU of the projection over the whole tensor."""
+    pr = W.WORKLOADS[4]["proj"]
+    M, K, H = pr["rows"], pr["dim"], pr["hidden"]
+    rng = np.random.Generator(np.random.PCG64(9600))
+    rsel = np.unique(np.concatenate([[0, 127, 128, M - 1], rng.integers(0, M, 4)]))
+    rs = torch.from_numpy(rsel).cuda()
+    say(f"gemm full size exact sums: {M} x {K} x {2 * H}, rows {rsel.tolist()}")
+    x = W.device_small_int_bf16((M, K), W.seed_for(4, "x"))
+    w = W.device_small_int_bf16((2 * H, K), W.seed_for(4, "weight"))
+    fused = rgg.gemm_geglu_bf16(x, w)
+    hx, hw = host(x[rs]), host(w)
+    assert_bitexact(host(fused[rs]), orc.gemm_geglu(hx, hw), "full size fused, exact sums")
+    plain = rgg.gemm_bf16_nt(x, w)
+    assert_bitexact(host(plain[rs]), orc.gemm_bf16(hx, hw), "full size projection, exact sums")
+    del plain, fused, x, w
+    say("gemm full size gaussian")
+    x = W.device_normal_bf16((M, K), W.seed_for(4, "x"))
+    w = W.device_normal_bf16((2 * H, K), W.seed_for(4, "weight"), 1.0 / np.sqrt(K))
+    plain = rgg.gemm_bf16_nt(x, w)
+    fused = rgg.gemm_geglu_bf16(x, w)
+    again = rgg.gelu_and_mul_bf16(plain)
+    bad = int((fused.view(torch.int16) != again.view(torch.int16)).sum())
+    say(f"full size fused vs gelu_and_mul(projection): {bad} of {fused.numel()} differ")
+    assert bad == 0
+    hx, hw = host(x[rs]), host(w)
+    check_projection_bound(hx, hw, host(plain[rs]), orc.gemm_bf16(hx, hw),
+                           "full size projection, gaussian")
+
+
+# ---------------------------------------------------------------------------
 # layouts, limits, graphs
 # ---------------------------------------------------------------------------
 

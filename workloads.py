@@ -14,7 +14,8 @@ no resolution, so the five workloads below are synthetic stand-ins:
   partial   x (2,4096,24,128), R=96 (32-column tail), 3-axis grid (1,64,64), dims 24/36/36
   geglu     gate/up 8192 x 12288, gate sigma 3, up sigma 1
   dit_layer fused qkv (4,8192,3*32*128); q/k strided views, R=128, grid (2,64,64),
-            dims 32/48/48; GEGLU 32768 x 8192
+            dims 32/48/48; GEGLU 32768 x 8192; the gate_up projection that feeds
+            it: x (32768, 4096) (model width H*D), weight (2*8192, 4096)
 
 Angles: for a 3-axis grid (T, Hg, Wg) token s = (t*Hg + h)*Wg + w, axis k of
 dimension d_k contributes d_k/2 half-angles pos_k * theta^(-2i/d_k); the R/2
@@ -23,8 +24,12 @@ cat(f, f), the layout a rotate-half RoPE pairs column j with j + R/2 in.
 Angles are computed in float64 and rounded once to float32.
 
 Random tensors: numpy PCG64 seeded with 1000*workload + tensor id (x/q 1,
-k 2, gate 3, up 4, qkv 5, extra 6), float32 N(0, sigma^2), converted to bf16
-by torch's round-to-nearest-even cast.  For full-size GPU runs the same
+k 2, gate 3, up 4, qkv 5, extra 6, weight 7), float32 N(0, sigma^2), converted
+to bf16 by torch's round-to-nearest-even cast; projection weights have sigma
+1/sqrt(K), so gates come out near N(0, 1).  Exact-sum inputs for the
+projection are small integers times a power of two (`small_int_bf16`): every
+partial sum of their products is a float32 integer multiple of that power, so
+any summation order gives the exact sum.  For full-size GPU runs the same
 recipe is drawn on the device by torch's generator (`device_normal_bf16`).
 """
 import numpy as np
@@ -47,10 +52,11 @@ WORKLOADS = {
     4: dict(name="dit_layer",
             rope=dict(B=4, S=8192, H=32, D=128, R=128, views=2, layout="qkv",
                       freqs=dict(kind="3axis", grid=(2, 64, 64), dims=(32, 48, 48))),
-            geglu=dict(rows=32768, hidden=8192, gate_sigma=1.0)),
+            geglu=dict(rows=32768, hidden=8192, gate_sigma=1.0),
+            proj=dict(rows=32768, dim=4096, hidden=8192)),
 }
 
-TENSOR_ID = dict(x=1, q=1, k=2, gate=3, up=4, qkv=5, extra=6)
+TENSOR_ID = dict(x=1, q=1, k=2, gate=3, up=4, qkv=5, extra=6, weight=7)
 
 
 def seed_for(workload, tensor):
@@ -123,6 +129,22 @@ def device_normal_bf16(shape, seed, sigma=1.0, device="cuda"):
     if sigma != 1.0:
         t.mul_(sigma)
     return t.to(torch.bfloat16)
+
+
+def small_int_bf16(shape, seed, bound=7, exp=-4):
+    """Integers uniform in [-bound, bound] times 2^exp, as bf16 bits (exact)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    a = rng.integers(-bound, bound + 1, size=shape).astype(np.float32) * np.float32(2.0 ** exp)
+    return f32_to_bf16_bits(a)
+
+
+def device_small_int_bf16(shape, seed, bound=7, exp=-4, device="cuda"):
+    """small_int_bf16's recipe drawn on the device by torch's generator."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    t = torch.randint(-bound, bound + 1, shape, generator=g, device=device, dtype=torch.int32)
+    return (t.to(torch.float32) * (2.0 ** exp)).to(torch.bfloat16)
 
 
 # ---------------------------------------------------------------------------
