@@ -329,8 +329,8 @@ int gemm_checks(const uint16_t *x, int64_t M, int64_t K, int64_t x_stride, const
     if (!aligned16(x) || !aligned16(w) || !aligned16(out) || x_stride % 8 || w_stride % 8 ||
         out_stride % 8)
         return RGG_ERR_ALIGN;
-    const int64_t mblocks = (M + 127) / 128, nblocks = H / 64;
-    if (M >= kMax32 || mblocks * nblocks >= ((int64_t)1 << 24) || H >= kMax32 / 2)
+    const int64_t mblocks = (M + 255) / 256, nblocks = (H + 127) / 128;
+    if (M >= kMax32 || K >= kMax32 || mblocks * nblocks >= ((int64_t)1 << 24) || H >= kMax32 / 2)
         return RGG_ERR_UNSUPPORTED;
     if (K > 0) {
         const int64_t xn[1] = {M}, xs[1] = {x_stride}, wn[1] = {2 * H}, ws[1] = {w_stride};
@@ -350,8 +350,9 @@ int gemm_checks(const uint16_t *x, int64_t M, int64_t K, int64_t x_stride, const
     p.out_stride = out_stride;
     p.M = M;
     p.H = (int32_t)H;
-    p.k_tiles = (int32_t)(K / 64);
-    p.div_nblocks = make_fastdiv((uint32_t)nblocks);
+    p.K = (int32_t)K;
+    p.mblocks = (uint32_t)mblocks;
+    p.nblocks = (uint32_t)nblocks;
     return RGG_OK;
 }
 

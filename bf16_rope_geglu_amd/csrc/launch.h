@@ -108,8 +108,9 @@ struct GemmParams {
     int64_t x_stride, w_stride, out_stride;
     int64_t M;
     int32_t H;
-    int32_t k_tiles;       // K / 64
-    FastDiv div_nblocks;   // divisor H / 64: workgroup -> (row block, column block)
+    int32_t K;             // a multiple of 64
+    uint32_t mblocks;      // ceil(M / 256) row blocks
+    uint32_t nblocks;      // ceil(H / 128) column blocks
 };
 
 // Launchers: enqueue on `stream`, return the hipError_t of the launch.

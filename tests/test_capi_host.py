@@ -192,9 +192,10 @@ def test_gemm_checks(lib, geglu):
     assert g(M=0) == OK
     assert g(N=0, os_=0, w=None) == OK
     assert g(M=1 << 31) == UNSUPPORTED                 # M >= 2^31
-    h = 1 << 13                                        # 2^7 column tiles of 64
+    h = 1 << 15                                        # 2^8 column blocks of 128
     assert g(M=1 << 24, N=h * (1 if geglu else 2),
-             os_=h * (1 if geglu else 2)) == UNSUPPORTED   # 2^17 x 2^7 = 2^24 tiles
+             os_=h * (1 if geglu else 2)) == UNSUPPORTED   # 2^16 x 2^8 = 2^24 blocks
+    assert g(K=1 << 31, xs=1 << 31, ws=1 << 31) == UNSUPPORTED   # K >= 2^31
 
 
 def test_gemm_plain_needs_whole_gate_up_pairs(lib):
