@@ -853,39 +853,42 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
 // accumulator, then either stored or turned into up * G(gate) in the
 // epilogue, so the (M, 2H) intermediate never goes to memory.
 //
-// A 256-thread workgroup (one wave per SIMD) computes a 256-row x 128-column
-// block of the output: per 32-wide slice of K it stages 256 rows of x and
-// the 128 gate rows plus the 128 matching up rows of W in LDS.  Wave
-// (wm, wn) owns rows wm*128 .. +127 and columns wn*64 .. +63 of both the
-// gate and the up block, so one lane holds the gate and the up accumulator
-// of the same (row, column).  W is the first MFMA operand and x the second,
-// so in a 32x32 block lane l holds output row l % 32 and, in its
+// A 512-thread workgroup (two waves per SIMD) computes a 256-row x
+// 128-column block of the output: per 32-wide slice of K it stages 256 rows
+// of x and the 128 gate rows plus the 128 matching up rows of W in LDS.
+// Wave (wm, wn) owns rows wm*128 .. +127 and columns wn*32 .. +31 of both
+// the gate and the up block, so one lane holds the gate and the up
+// accumulator of the same (row, column).  W is the first MFMA operand and x
+// the second, so in a 32x32 block lane l holds output row l % 32 and, in its
 // accumulators v, output columns (v / 4) * 8 + (l / 32) * 4 + v % 4.
 // Operands: lane l supplies row l % 32 of W or of x and the 8 consecutive k
-// at (l / 32) * 8.
+// at (l / 32) * 8.  Two waves per SIMD matter here: a wave that issues a
+// global load waits until the CU's address unit takes it, and the other
+// wave on the SIMD keeps the matrix pipe busy meanwhile.
 //
 // Staging uses the direct global-to-LDS load (16 bytes per lane, one 1 KiB
 // run of LDS per instruction: 16 rows of 64 bytes), so the slices never pass
 // through registers.  Rows are unpadded; the 16-byte chunk c of row r sits
-// at chunk c ^ ((r / 2) % 4), which puts the 8 rows read by one LDS cycle of
-// an operand fetch on disjoint banks.  Four stages: the loads of slice
-// kt + 3 are issued while slice kt is multiplied, so a load has three
-// slices of products to arrive (the first touch of a line goes to HBM).
-// Before the barrier that ends slice kt, each wave waits only for its own
-// loads of slice kt + 1 (loads complete in order).
+// at chunk c ^ ((r / 4) % 4).  A 16-byte LDS read serves 16 lanes per cycle
+// from 64 four-byte banks; in an operand fetch those lanes read 16
+// consecutive rows at one logical chunk, and the swizzle puts them on 16
+// disjoint 16-byte bank groups (row r starts at group 4 (r % 4)).  Four
+// stages: the loads of slice kt + 3 are issued while slice kt is
+// multiplied, so a load has three slices of products to arrive (the first
+// touch of a line goes to HBM).  Before the barrier that ends slice kt, each
+// wave waits only for its own loads of slice kt + 1 (loads complete in
+// order).
 //
-// Per slice each wave issues 32 products in 2 steps of 16; the LDS reads of
-// the next step's fragments (into the other register set) and the slice's
-// global loads are interleaved with the products of the current step.
-//
-// Workgroups go to the 8 XCDs round robin; the block index is remapped so
-// that each XCD gets one contiguous run of tiles, and the run is walked in
-// groups of 8 row blocks (column block outer), so the tiles an XCD works on
-// at one time share rows of x and of W in its L2.
+// The workgroups are persistent (one per CU) and walk the tiles; the block
+// order is remapped so that each XCD (workgroups go to the 8 XCDs round
+// robin) gets one contiguous run of tiles, walked in groups of 8 row blocks
+// with the column block outer, so the tiles an XCD works on at one time
+// share rows of x and of W in its L2.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+constexpr int kGemmThreads = 512;
 constexpr int kGemmBM = 256;              // rows of x per workgroup
 constexpr int kGemmBN = 128;              // gate (and up) columns per workgroup
 constexpr int kGemmBK = 32;               // K slice per stage (64-byte rows)
@@ -893,31 +896,21 @@ constexpr int kGemmStages = 4;
 constexpr int kGemmLutBytes = kLutEntries * 2;       // GELU table at LDS offset 0
 constexpr int kGemmOpBytes = 256 * kGemmBK * 2;      // one staged operand (x or W)
 constexpr int kGemmStageBytes = 2 * kGemmOpBytes;
-constexpr int kGemmEpLd = 72;             // epilogue rows, elements (padded)
 constexpr size_t kGemmLds = kGemmLutBytes + kGemmStages * kGemmStageBytes;
 constexpr uint32_t kGemmGroupM = 8;
 static_assert(kGemmLds <= 160 * 1024, "LDS of one CU");
 static_assert(kGemmLutBytes % 1024 == 0, "stages start on a 1 KiB boundary");
-static_assert(4 * 128 * kGemmEpLd * 2 <= kGemmStages * kGemmStageBytes, "epilogue fits the stages");
-static_assert(kLutEntries % 8 == 0 && kLutEntries / 8 <= 2 * 256, "table: two vectors per lane");
+static_assert(8 * 128 * 32 * 2 <= 2 * kGemmStageBytes, "epilogue blocks fit stages 2-3");
+static_assert(kLutEntries % 8 == 0 && kLutEntries / 8 <= kGemmThreads, "table: one vector per lane");
 
 __device__ __forceinline__ uint32_t bf16_of(float v) { return rne_pack(v, 0.0f) & 0xFFFFu; }
 
-// Scheduling groups (LLVM AMDGPU sched_group_barrier masks).
-constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
-#define RGG_SG(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 #define RGG_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-template <bool Geglu>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_gate_up_kernel(GemmParams p)
+// Tile t of T (in launch order) -> (row block, column block): the XCD run
+// remap, then groups of kGemmGroupM row blocks with the column block outer.
+__device__ __forceinline__ void gemm_tile(const GemmParams &p, uint32_t t, int64_t &m0, int32_t &n0)
 {
-    // [GELU table][stage 0: x | W] .. [stage 3: x | W]
-    extern __shared__ __align__(16) uint8_t gsm[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    uint32_t t = blockIdx.x;
     const uint32_t T = p.mblocks * p.nblocks;
     if ((T & 7) == 0)
         t = (t & 7) * (T >> 3) + (t >> 3);
@@ -925,172 +918,213 @@ void gemm_gate_up_kernel(GemmParams p)
     const uint32_t grp = t / span, r = t - grp * span;
     const uint32_t first = grp * kGemmGroupM;
     const uint32_t gm = min(kGemmGroupM, p.mblocks - first);
-    const uint32_t mb = first + r % gm, nb = r / gm;
-    const int64_t m0 = (int64_t)mb * kGemmBM;
-    const int32_t n0 = (int32_t)nb * kGemmBN;
+    m0 = (int64_t)(first + r % gm) * kGemmBM;
+    n0 = (int32_t)(r / gm) * kGemmBN;
+}
 
-    // The GELU table goes to LDS now; it is read after the main loop, whose
-    // barriers order these writes before those reads.
-    if (Geglu) {
-        constexpr int nv = kLutEntries / 8;
-        const v4u *src = reinterpret_cast<const v4u *>(g_gelu_lut);
-        v4u *dst = reinterpret_cast<v4u *>(gsm);
-        dst[tid] = src[tid];
-        if (tid + 256 < nv)
-            dst[tid + 256] = src[tid + 256];
-    }
+template <bool Geglu>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_gate_up_kernel(GemmParams p)
+{
+    // [GELU table][stage 0: x | W] .. [stage 3: x | W]
+    extern __shared__ __align__(16) uint8_t gsm[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wv >> 2, wn = wv & 3;
+    const uint32_t T = p.mblocks * p.nblocks;
 
-    // Wave w stages row groups 4w .. 4w + 3 (16 rows each) of the x tile and
-    // of the W tile: lane i of group g brings row 16g + i / 4, logical chunk
-    // (i % 4) ^ ((i / 8) % 4), to LDS chunk i % 4 of that row.  Rows past M
-    // re-read row M-1 and columns past H re-read column H-1 (not stored).
-    const uint16_t *gx[4], *gw[4];
+    // The GELU table goes to LDS now; it is read in the epilogues, after
+    // barriers that order these writes before those reads.
+    if (Geglu && tid < (int)(kLutEntries / 8))
+        reinterpret_cast<v4u *>(gsm)[tid] = reinterpret_cast<const v4u *>(g_gelu_lut)[tid];
+
+    // Wave w stages row groups 2w, 2w + 1 (16 rows each) of the x tile and of
+    // the W tile (waves 0-3: gate rows, 4-7: up rows): lane i of group g
+    // brings row 16g + i / 4, logical chunk (i % 4) ^ ((i / 16) % 4), to LDS
+    // chunk i % 4 of that row.  The loads address memory as a wave-uniform
+    // base (SGPRs) plus a per-lane 32-bit byte offset fixed for the tile;
+    // offsets stay below 256 row strides, so strides are limited to 2^23
+    // elements.  Rows past M re-read row M-1 and columns past H re-read
+    // column H-1 (not stored).  (The lane index passes through an empty asm
+    // statement so that the compiler recomputes the offsets per tile instead
+    // of keeping loop-invariant copies alive across the tile loop.)
+    uint32_t ox[2], ow[2];
+    const uint16_t *bx = p.x, *bw = p.w;
+    auto point = [&](int64_t m0, int32_t n0) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        bx = p.x + m0 * p.x_stride;
+        bw = p.w + ((wv < 4 ? 0 : (int64_t)p.H) + n0) * p.w_stride;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = 64 * wave + 16 * j + (lane >> 2);
-        const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
-        const int64_t m = min(m0 + row, p.M - 1);
-        const int32_t c = min(n0 + (row & (kGemmBN - 1)), p.H - 1);
-        const int64_t wr = row < kGemmBN ? c : (int64_t)p.H + c;
-        gx[j] = p.x + m * p.x_stride + chunk * 8;
-        gw[j] = p.w + wr * p.w_stride + chunk * 8;
-    }
-    // One load instruction: row group idx % 4 of x (idx < 4) or of W.  It is
-    // written out (M0 holds the LDS address) rather than left to the
+        for (int j = 0; j < 2; ++j) {
+            const int row = 32 * wv + 16 * j + (ln >> 2);
+            const int chunk = (ln & 3) ^ ((ln >> 4) & 3);
+            const uint32_t m = (uint32_t)(min(m0 + row, p.M - 1) - m0);
+            const uint32_t c = (uint32_t)(min(n0 + (row & (kGemmBN - 1)), p.H - 1) - n0);
+            ox[j] = m * (uint32_t)p.x_stride * 2u + chunk * 16;
+            ow[j] = c * (uint32_t)p.w_stride * 2u + chunk * 16;
+        }
+    };
+    // One load instruction: row group 2w + (idx & 1) of x (idx < 2) or of W.
+    // It is written out (M0 holds the LDS address) rather than left to the
     // compiler, which does not know which LDS bytes a direct load writes and
     // would make every later LDS read wait for every load in flight; here
     // the ordering is explicit: "vmcnt" waits before each barrier, and a
     // stage is only reloaded after the barrier that ends its last reads.
     // The instruction has no register result.
-    const uint32_t lds0 = (uint32_t)(uintptr_t)gsm + kGemmLutBytes + wave * 4 * 1024;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)gsm + kGemmLutBytes + wv * 2 * 1024;
     auto dma1 = [&](int kt, int st, int idx) {
-        const int j = idx & 3;
-        const uint16_t *src = (idx < 4 ? gx[j] : gw[j]) + (int64_t)kt * kGemmBK;
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(
-            lds0 + st * kGemmStageBytes + (idx < 4 ? 0 : kGemmOpBytes) + j * 1024);
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     :: "v"(src), "s"(dst) : "memory");
+        const int j = idx & 1;
+        const uint16_t *base = (idx < 2 ? bx : bw) + (int64_t)kt * kGemmBK;
+        const uint32_t off = idx < 2 ? ox[j] : ow[j];
+        const uint32_t dst = lds0 + st * kGemmStageBytes + (idx < 2 ? 0 : kGemmOpBytes) + j * 1024;
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(off), "s"(base), "s"(dst) : "memory");
     };
     auto fetch = [&](int kt, int st) {
 #pragma unroll
-        for (int idx = 0; idx < 8; ++idx)
+        for (int idx = 0; idx < 4; ++idx)
             dma1(kt, st, idx);
     };
 
-    f32x16 acc[4][4];  // [x row block][gate 0, gate 1, up 0, up 1]
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[a][b][v] = 0.0f;
+    f32x16 acc[4][2];  // [x row block][gate, up]
 
-    // Operand fragments, double buffered in registers (set 0 / set 1).
+    // Operand fragments, double buffered in registers (set 0 / set 1):
+    // 4 of x, then the gate and the up fragment of W.
     const int ra = (wm * 128 + (lane & 31)) * 64;
-    const int rb = (wn * 64 + (lane & 31)) * 64;
-    bf16x8 fa[2][4], fb[2][4];
-    // One fragment: x rows (idx < 4) or W rows (gate 0, gate 1, up 0, up 1).
+    const int rb = (wn * 32 + (lane & 31)) * 64;
+    bf16x8 fa[2][4], fb[2][2];
     auto frag1 = [&](int st, int ks, int set, int idx) {
         const uint8_t *sx = gsm + kGemmLutBytes + st * kGemmStageBytes;
-        const int ch = ((2 * ks + (lane >> 5)) ^ ((lane >> 1) & 3)) * 16;
+        const int ch = ((2 * ks + (lane >> 5)) ^ ((lane >> 2) & 3)) * 16;
         if (idx < 4)
             fa[set][idx] = *reinterpret_cast<const bf16x8 *>(sx + ra + idx * 32 * 64 + ch);
         else
             fb[set][idx - 4] = *reinterpret_cast<const bf16x8 *>(
-                sx + kGemmOpBytes + rb + (((idx - 4) >> 1) * kGemmBN + ((idx - 4) & 1) * 32) * 64 + ch);
+                sx + kGemmOpBytes + rb + (idx - 4) * kGemmBN * 64 + ch);
     };
     auto mma1 = [&](int set, int idx) {
-        const int i = idx >> 2, j = idx & 3;
+        const int i = idx >> 1, j = idx & 1;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
     };
 
-    // Each wave issues 8 loads per slice.  The instruction order inside a
-    // slice is fixed by scheduling fences, one memory instruction after each
-    // product: products 0-15 (set 0) carry the 8 fragment reads of set 1 and
-    // 4 loads of slice kt + 3 (after products 2, 6, 10, 14); products 16-23
-    // (set 1) carry 2 more loads; then the wave waits for its loads of slice
-    // kt + 1 ("vmcnt(14)": slice kt + 2 and 6 loads of kt + 3 may still be in
-    // flight; loads complete in order) and passes the barrier; products
-    // 24-31 carry the 8 fragment reads of the next slice's set 0 and the
-    // last 2 loads.  Loads are spread out so that the address unit, shared
-    // by the 4 waves, never holds up the issue of a product for long.
+    // The workgroup walks tiles blockIdx.x, + gridDim.x, ... (one workgroup
+    // per CU).  The first two slices of the next tile are requested before
+    // the epilogue of the current one, so their latency hides under it.
     const int KT = p.K / kGemmBK;
+    uint32_t tile = blockIdx.x;
+    int64_t m0;
+    int32_t n0;
+    gemm_tile(p, tile, m0, n0);
+    point(m0, n0);
     if (KT > 0) {
         fetch(0, 0);
         fetch(min(1, KT - 1), 1);
         fetch(min(2, KT - 1), 2);
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     }
     __syncthreads();
-    if (KT > 0) {
+    for (;;) {
 #pragma unroll
-        for (int idx = 0; idx < 8; ++idx)
-            frag1(0, 0, 0, idx);
-        RGG_FENCE();
-        for (int kt = 0; kt + 1 < KT; ++kt) {
-            const int st = kt & 3;
-            const int kn = min(kt + 3, KT - 1), sn = (kt + 3) & 3;
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                mma1(0, k);
-                if (k < 8)
-                    frag1(st, 1, 1, k);
-                if ((k & 3) == 2)
-                    dma1(kn, sn, k >> 2);
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[a][b][v] = 0.0f;
+
+        // Each wave issues 4 loads per slice.  Instruction order inside a
+        // slice (fixed by scheduling fences): products 0-7 (set 0) carry the
+        // 6 fragment reads of set 1 and 2 loads of slice kt + 3; products
+        // 8-11 (set 1) carry the other 2 loads; then the wave waits for its
+        // loads of slice kt + 1 ("vmcnt(8)": slices kt + 2 and kt + 3 may
+        // still be in flight; loads complete in order) and passes the
+        // barrier; products 12-15 carry the 6 fragment reads of the next
+        // slice's set 0.
+        if (KT > 0) {
+#pragma unroll
+            for (int idx = 0; idx < 6; ++idx)
+                frag1(0, 0, 0, idx);
+            RGG_FENCE();
+            for (int kt = 0; kt + 1 < KT; ++kt) {
+                const int st = kt & 3;
+                const int kn = min(kt + 3, KT - 1), sn = (kt + 3) & 3;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    mma1(0, k);
+                    if (k < 6)
+                        frag1(st, 1, 1, k);
+                    if (k == 2 || k == 6)
+                        dma1(kn, sn, k >> 2);
+                    RGG_FENCE();
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    mma1(1, k);
+                    if (k == 0 || k == 2)
+                        dma1(kn, sn, 2 + (k >> 1));
+                    RGG_FENCE();
+                }
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                __builtin_amdgcn_s_barrier();
                 RGG_FENCE();
+#pragma unroll
+                for (int k = 4; k < 8; ++k) {
+                    if (k < 7) {
+                        frag1((kt + 1) & 3, 0, 0, 2 * (k - 4));
+                        frag1((kt + 1) & 3, 0, 0, 2 * (k - 4) + 1);
+                    }
+                    mma1(1, k);
+                    RGG_FENCE();
+                }
             }
+            const int st = (KT - 1) & 3;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                mma1(1, k);
-                if ((k & 3) == 2)
-                    dma1(kn, sn, 4 + (k >> 2));
+                mma1(0, k);
+                if (k < 6)
+                    frag1(st, 1, 1, k);
                 RGG_FENCE();
             }
-            asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            RGG_FENCE();
 #pragma unroll
-            for (int k = 8; k < 16; ++k) {
-                frag1((kt + 1) & 3, 0, 0, k - 8);
+            for (int k = 0; k < 8; ++k)
                 mma1(1, k);
-                if ((k & 3) == 2)
-                    dma1(kn, sn, 6 + ((k - 8) >> 2));
-                RGG_FENCE();
-            }
         }
-        const int st = (KT - 1) & 3;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            mma1(0, k);
-            if (k < 8)
-                frag1(st, 1, 1, k);
-            RGG_FENCE();
-        }
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-            mma1(1, k);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // every wave is done with the operand stages
 
-    // Epilogue: round each accumulator to bf16 (the projection's output),
-    // then keep it, or form rne(up * G(gate)).  Each wave writes its 128 x 64
-    // block of results to LDS as rows (four adjacent columns per 8-byte
-    // write), then reads it back as 16-byte vectors, eight lanes per 128-byte
-    // row, for whole-line global stores.  The plain product does this twice:
-    // gate columns, then up columns (H further along the row).  H is a
-    // multiple of 64, so a wave's block is wholly inside [0, H) or outside.
-    __syncthreads();  // every wave is done with the operand tiles
-    const uint16_t *lut = reinterpret_cast<const uint16_t *>(gsm);
-    uint16_t *ep = reinterpret_cast<uint16_t *>(gsm + kGemmLutBytes) + wave * 128 * kGemmEpLd;
-    const int32_t cbase = n0 + wn * 64;
-    const bool live = cbase < p.H;
+        const int64_t cm0 = m0;
+        const int32_t cn0 = n0;
+        const uint32_t next = tile + gridDim.x;
+        const bool more = next < T;
+        if (more) {
+            gemm_tile(p, next, m0, n0);
+            point(m0, n0);
+            if (KT > 0) {
+                fetch(0, 0);
+                fetch(min(1, KT - 1), 1);
+            }
+        }
+
+        // Epilogue: round each accumulator to bf16 (the projection's
+        // output), then keep it, or form rne(up * G(gate)).  Each wave writes
+        // its 128 x 32 block of results to its 8 KiB of stages 2-3 as 64-byte
+        // rows (16-byte chunk c of row r at chunk c ^ ((r / 4) % 4); four
+        // adjacent columns per 8-byte write), then reads it back as 16-byte
+        // vectors, four lanes per row, for 64-byte global stores.  The plain
+        // product does this twice: gate columns, then up columns (H further
+        // along the row).  H is a multiple of 64, so a wave's 32 columns are
+        // wholly inside [0, H) or outside.
+        const uint16_t *lut = reinterpret_cast<const uint16_t *>(gsm);
+        uint8_t *ep = gsm + kGemmLutBytes + 2 * kGemmStageBytes + wv * 8192;
+        int el = lane;
+        asm volatile("" : "+v"(el));
+        const int32_t cbase = cn0 + wn * 32;
+        const bool live = cbase < p.H;
 #pragma unroll
-    for (int half = 0; half < (Geglu ? 1 : 2); ++half) {
+        for (int half = 0; half < (Geglu ? 1 : 2); ++half) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     uint32_t w0, w1;
@@ -1100,8 +1134,8 @@ void gemm_gate_up_kernel(GemmParams p)
                         bool general = false;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            g[e] = bf16_of(acc[i][cb][q * 4 + e]);
-                            u[e] = bf16_of(acc[i][2 + cb][q * 4 + e]);
+                            g[e] = bf16_of(acc[i][0][q * 4 + e]);
+                            u[e] = bf16_of(acc[i][1][q * 4 + e]);
                             G[e] = __uint_as_float(gelu_common(g[e], lut));
                             general |= (g[e] & 0x7FFFu) - 0x0100u >= kLutHi - 0x0100u;
                         }
@@ -1113,30 +1147,43 @@ void gemm_gate_up_kernel(GemmParams p)
                         w0 = rne_pack(bf_lo(u[0]) * G[0], bf_lo(u[1]) * G[1]);
                         w1 = rne_pack(bf_lo(u[2]) * G[2], bf_lo(u[3]) * G[3]);
                     } else {
-                        const f32x16 &a = acc[i][2 * half + cb];
+                        const f32x16 &a = acc[i][half];
                         w0 = rne_pack(a[q * 4 + 0], a[q * 4 + 1]);
                         w1 = rne_pack(a[q * 4 + 2], a[q * 4 + 3]);
                     }
-                    const int r = i * 32 + (lane & 31), c = cb * 32 + q * 8 + (lane >> 5) * 4;
-                    *reinterpret_cast<uint2 *>(ep + r * kGemmEpLd + c) = make_uint2(w0, w1);
+                    const int r = i * 32 + (el & 31);
+                    *reinterpret_cast<uint2 *>(ep + r * 64 + ((q ^ ((r >> 2) & 3)) << 4) +
+                                               (el >> 5) * 8) = make_uint2(w0, w1);
                 }
             }
-        }
-        __syncthreads();
-        uint16_t *ob = p.out + (half ? p.H : 0) + cbase;
+            // A wave reads back only its own block, and LDS operations of
+            // one wave complete in order: no barrier (which would also wait
+            // for the next tile's loads).
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            uint16_t *ob = p.out + (half ? p.H : 0) + cbase;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int rr = (lane >> 3) + 8 * k, cv = lane & 7;
-            const v4u val = *reinterpret_cast<const v4u *>(ep + rr * kGemmEpLd + cv * 8);
-            const int64_t row = m0 + wm * 128 + rr;
-            if (live && row < p.M)
-                *reinterpret_cast<v4u *>(ob + row * p.out_stride + cv * 8) = val;
+            for (int k = 0; k < 8; ++k) {
+                const int rr = (el >> 2) + 16 * k, cv = el & 3;
+                const v4u val = *reinterpret_cast<const v4u *>(ep + rr * 64 + ((cv ^ ((rr >> 2) & 3)) << 4));
+                const int64_t row = cm0 + wm * 128 + rr;
+                if (live && row < p.M)
+                    *reinterpret_cast<v4u *>(ob + row * p.out_stride + cv * 8) = val;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
-        if (!Geglu && half == 0)
-            __syncthreads();
+        if (!more)
+            break;
+        tile = next;
+        // Every wave has left its block area (stages 2-3): slice 2 of the new
+        // tile may go to stage 2 once slices 0 and 1 (and this tile's stores)
+        // are in; the second barrier makes slices 0 and 1 visible to all.
+        __builtin_amdgcn_s_barrier();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (KT > 0)
+            fetch(min(2, KT - 1), 2);
+        __builtin_amdgcn_s_barrier();
     }
 }
-#undef RGG_SG
 #undef RGG_FENCE
 
 }  // namespace
@@ -1269,7 +1316,15 @@ hipError_t launch_gemm_gate_up(const GemmParams &p, bool geglu, hipStream_t stre
     });
     if (attr != hipSuccess)
         return attr;
-    const dim3 grid(p.mblocks * p.nblocks), block(256);
+    // One workgroup per CU (the LDS use allows no more), each walking tiles.
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    const uint32_t tiles = p.mblocks * p.nblocks;
+    const dim3 grid(min(tiles, (uint32_t)max(cus, 1))), block(kGemmThreads);
     if (geglu)
         hipLaunchKernelGGL(gemm_gate_up_kernel<true>, grid, block, kGemmLds, stream, p);
     else
