@@ -14,6 +14,12 @@ step / mean step time (GB/s, 1e9 bytes).  Every kernel is also bracketed by
 HIP events on the stream it runs on, which gives each one's mean launch
 duration and its algorithmic GB/s; `roofline` reports the dominant kernel.
 
+`projection` times the gate_up projection of the same layer on the matrix
+cores, x (32768, 4096) times W (2 x 8192, 4096): GEGLU fused into its
+epilogue, the plain projection, the unfused pair, and the platform library
+GEMM followed by gelu_and_mul_bf16 for comparison (TFLOP/s against the
+2.5 PFLOP/s dense bf16 peak).  It is outside the step and its `value`.
+
 `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload (16384 tokens, 8192 GEGLU rows): `value` on one thread, and
 `all_cores` with the sample split over every core the process may use.  `roofline.traffic` comes from the committed rocprofv3
@@ -24,6 +30,10 @@ changed since the counters were taken.
 turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs (DIR/fetch, DIR/write)
 into that summary; --calibration-copy adds a plain device copy of known size
 to each step so the same runs calibrate the counters.
+
+    python bench.py --projection [--calibration-copy]
+times only the gate_up projection entry points (and adds the calibration
+copy); --pmc-set projection summarises counters of such runs.
 
     python bench.py --sweep
 prints a markdown table of every kernel on every workload with cold caches
@@ -163,6 +173,65 @@ def run_gpu(args):
         "wid": wid, "ms_per_step": ms_per_step, "wall_s": wall, "step_bytes": step_bytes,
         "kernels": kernels, "dominant": dominant, "shape": (B, S, H, D, R, rows, hidden),
     }
+
+
+# ---------------------------------------------------------------------------
+# the gate_up projection with GEGLU in its epilogue (matrix cores)
+# ---------------------------------------------------------------------------
+
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def run_projection(reps=10, warmup=2):
+    """The dit_layer projection, x (32768, 4096) times W (2 x 8192, 4096):
+    gemm_geglu_bf16 (fused), gemm_bf16_nt alone, gemm_bf16_nt followed by
+    gelu_and_mul_bf16 (the unfused path), and torch.matmul (the platform's
+    library GEMM) followed by gelu_and_mul_bf16, for comparison.  Mean of
+    `reps` launches between HIP events on the launch stream; TFLOP/s counts
+    2 M K (2 H) multiply-adds."""
+    import torch
+
+    import bf16_rope_geglu_amd as rgg
+    import workloads as W
+
+    pr = W.WORKLOADS[4]["proj"]
+    M, K, H = pr["rows"], pr["dim"], pr["hidden"]
+    dev = torch.device("cuda:0")
+    x = W.device_normal_bf16((M, K), W.seed_for(4, "x"), device=dev)
+    w = W.device_normal_bf16((2 * H, K), W.seed_for(4, "weight"), 1.0 / K ** 0.5, dev)
+    out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    proj = torch.empty((M, 2 * H), dtype=torch.bfloat16, device=dev)
+    rgg.prepare_device(0)
+    flops = 2.0 * M * K * 2 * H
+    cases = [
+        ("gemm_geglu_bf16", lambda: rgg.gemm_geglu_bf16(x, w, out)),
+        ("gemm_bf16_nt", lambda: rgg.gemm_bf16_nt(x, w, proj)),
+        ("gemm_bf16_nt + gelu_and_mul_bf16",
+         lambda: (rgg.gemm_bf16_nt(x, w, proj), rgg.gelu_and_mul_bf16(proj, out))),
+        ("torch.matmul + gelu_and_mul_bf16 (comparison)",
+         lambda: (torch.matmul(x, w.t(), out=proj), rgg.gelu_and_mul_bf16(proj, out))),
+    ]
+    res = {}
+    for name, fn in cases:
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        tf = flops / (us * 1e-6) / 1e12
+        res[name] = {"us": round(us, 1), "TFLOPs": round(tf, 1),
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del x, w, out, proj
+    torch.cuda.empty_cache()
+    return {"shape": {"M": M, "K": K, "hidden": H}, "flops": flops,
+            "intermediate_bytes_avoided": 2 * M * 2 * H * 2, "peak_TFLOPs": PEAK_BF16_TFLOPS,
+            "results": res}
 
 
 # ---------------------------------------------------------------------------
@@ -307,6 +376,13 @@ def run_sweep(reps=40, touch=2 << 30):
                              stream_us(algo["geglu"], 2)))
         torch.cuda.empty_cache()
 
+    proj = run_projection()
+    print(f"Projection {proj['shape']} (matrix cores, {proj['flops']:.3e} flop per launch)")
+    print("| entry point | us per launch | TFLOP/s | % of 2.5 PFLOP/s |")
+    print("|---|---|---|---|")
+    for n, r in proj["results"].items():
+        print(f"| {n} | {r['us']:.1f} | {r['TFLOPs']:.1f} | {100 * r['frac']:.1f} |")
+    print()
     print("| workload | entry point | algorithmic bytes | buffer sets | us per launch | GB/s "
           "| % of 8 TB/s | stream reference us (% of 8 TB/s) | kernel vs stream |")
     print("|---|---|---|---|---|---|---|---|---|")
@@ -404,12 +480,16 @@ def _per_dispatch(rows, counter, symbol):
 
 KNOWN_KERNELS = ("rope_cossin_kernel", "rope_cossin_grid_kernel", "rope_rotate_half_kernel",
                  "rope_rotate_half_lane_kernel", "gelu_and_mul_kernel", "build_gelu_table_kernel",
-                 "stream_ref_kernel")
+                 "gemm_gate_up_kernel", "stream_ref_kernel")
 
 
 def _short_kernel(name):
     """The kernel's own name inside a demangled symbol such as
-    `rgg::(anonymous namespace)::rope_rotate_half_kernel<true, true>(...)`."""
+    `rgg::(anonymous namespace)::rope_rotate_half_kernel<true, true>(...)`;
+    the projection kernel keeps its template argument (true: GEGLU epilogue)."""
+    m = re.search(r"gemm_gate_up_kernel\s*<\s*(true|false)\s*>", name)
+    if m:
+        return f"gemm_gate_up_kernel<{m.group(1)}>"
     for v in KNOWN_KERNELS:
         if re.search(r"(?:^|::|\s)" + v + r"\s*[<(]", name):
             return v
@@ -459,7 +539,22 @@ def trace_summary(d, out, command):
     print(text)
 
 
-def pmc_summary(d, out, command=""):
+PROJ_SYMBOL = {
+    "projection_geglu": "gemm_gate_up_kernel<true>",
+    "projection_plain": "gemm_gate_up_kernel<false>",
+}
+
+
+def projection_algo_bytes():
+    """x and W read once, the output written once (dit_layer projection)."""
+    import workloads as W
+    pr = W.WORKLOADS[4]["proj"]
+    M, K, H = pr["rows"], pr["dim"], pr["hidden"]
+    inputs = 2 * M * K + 2 * 2 * H * K
+    return {"projection_geglu": inputs + 2 * M * H, "projection_plain": inputs + 2 * M * 2 * H}
+
+
+def pmc_summary(d, out, command="", which="step"):
     fetch = _counter_rows(os.path.join(d, "fetch"))
     write = _counter_rows(os.path.join(d, "write"))
     copy_sym = "copyBuffer"   # the HIP runtime's device-to-device copy kernel
@@ -472,9 +567,13 @@ def pmc_summary(d, out, command=""):
     w_scale = COPY_BYTES / (1024 * sorted(big_w)[len(big_w) // 2]) if big_w else None
     res["fetch_scale"] = f_scale
     res["write_scale"] = w_scale
-    lines = ["# HBM traffic per dispatch from rocprofv3 counters (dit_layer workload)", "",
+    title = ("the gate_up projection of the dit_layer workload" if which == "projection"
+             else "dit_layer workload")
+    lines = [f"# HBM traffic per dispatch from rocprofv3 counters ({title})", "",
              f"Commands: `{command}`", ""]
-    for n, sym in KERNEL_SYMBOL.items():
+    symbols = PROJ_SYMBOL if which == "projection" else KERNEL_SYMBOL
+    algo = projection_algo_bytes() if which == "projection" else {}
+    for n, sym in symbols.items():
         f = _per_dispatch(fetch, "FETCH_SIZE", sym)
         w = _per_dispatch(write, "WRITE_SIZE", sym)
         if not f or not w:
@@ -484,7 +583,8 @@ def pmc_summary(d, out, command=""):
         wb = wk * 1024 * (w_scale or 1.0)
         res[n] = {"fetch_kib": fk, "write_kib": wk, "bytes": fb + wb, "dispatches": len(f)}
         lines.append(f"- {sym}: FETCH_SIZE {fk:.0f} KiB, WRITE_SIZE {wk:.0f} KiB per dispatch "
-                     f"(median of {len(f)}); scaled total {(fb + wb) / 1e9:.4f} GB")
+                     f"(median of {len(f)}); scaled total {(fb + wb) / 1e9:.4f} GB"
+                     + (f" against {algo[n] / 1e9:.4f} GB algorithmic" if n in algo else ""))
     lines += ["", f"Copy calibration ({COPY_BYTES} bytes each way): fetch scale {f_scale}, "
               f"write scale {w_scale}", "", "```json", json.dumps(res, indent=1), "```", ""]
     with open(out, "w") as f:
@@ -514,9 +614,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit_layer", choices=["dit_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-projection", action="store_true",
+                    help="skip the gate_up projection timings in the JSON line")
     ap.add_argument("--calibration-copy", action="store_true")
     ap.add_argument("--pmc-summary", metavar="DIR")
     ap.add_argument("--pmc-out", metavar="FILE", default=TRAFFIC_SUMMARY)
+    ap.add_argument("--pmc-set", choices=["step", "projection"], default="step")
+    ap.add_argument("--projection", action="store_true",
+                    help="time only the gate_up projection entry points (JSON)")
     ap.add_argument("--trace-summary", metavar="DIR")
     ap.add_argument("--trace-out", metavar="FILE")
     ap.add_argument("--command", default="", help="command line recorded in summaries")
@@ -525,7 +630,19 @@ def main():
     args = ap.parse_args()
 
     if args.pmc_summary:
-        pmc_summary(args.pmc_summary, args.pmc_out, args.command)
+        pmc_summary(args.pmc_summary, args.pmc_out, args.command, args.pmc_set)
+        return 0
+    if args.projection:
+        import torch
+        torch.cuda.set_device(0)
+        res = run_projection()
+        if args.calibration_copy:
+            src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps(res), flush=True)
         return 0
     if args.trace_summary:
         trace_summary(args.trace_summary, args.trace_out, args.command)
@@ -567,6 +684,8 @@ def main():
         "kernels": res["kernels"],
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
     }
+    if not args.no_projection:
+        line["projection"] = run_projection()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(res["wid"])
     print(json.dumps(line), flush=True)
