@@ -357,3 +357,23 @@ def test_size_limits_are_refused_before_any_launch(lib):
     assert cossin(lib, S=1 << 14, B=1 << 14, R=32) == UNSUPPORTED        # S*B*R/4 = 2^31
     assert grid(lib, B=1, T=1 << 11, Hg=1 << 10, Wg=1 << 10) == UNSUPPORTED  # S = 2^31
     assert grid(lib, B=1 << 12, T=1, Hg=1 << 10, Wg=1 << 9, d=(16, 8, 8)) == UNSUPPORTED
+
+
+def test_projection_bytes_and_trace_names():
+    """The projection's algorithmic bytes (x and W once, output once) and the
+    trace summary's names for its two template instances."""
+    sys.path.insert(0, ROOT)
+    import bench
+    b = bench.projection_algo_bytes()
+    x, w = 2 * 32768 * 4096, 2 * 16384 * 4096
+    assert b == {"projection_geglu": x + w + 2 * 32768 * 8192,
+                 "projection_plain": x + w + 2 * 32768 * 16384}
+    assert bench._short_kernel(
+        "void rgg::(anonymous namespace)::gemm_gate_up_kernel<true>(rgg::GemmParams)") \
+        == "gemm_gate_up_kernel<true>"
+    assert bench._short_kernel(
+        "void rgg::(anonymous namespace)::gemm_gate_up_kernel<false>(rgg::GemmParams)") \
+        == "gemm_gate_up_kernel<false>"
+    assert bench._short_kernel(
+        "void rgg::(anonymous namespace)::rope_rotate_half_kernel<true, false>(rgg::RopeParams)") \
+        == "rope_rotate_half_kernel"
