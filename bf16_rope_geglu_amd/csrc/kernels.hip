@@ -142,7 +142,7 @@ __device__ __forceinline__ uint32_t bf16_from_double(double v)
 }
 
 // ---------------------------------------------------------------------------
-// (a1) cos/sin tables                             [ERNIE-fuse §1]
+// Cos/sin tables                             [ERNIE-fuse §1]
 //
 // One lane per 8 consecutive rotary columns of one table row: two 16-byte
 // angle loads, eight fp32 sincosf, two 16-byte stores.  sincosf is accurate
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
 }
 
 // ---------------------------------------------------------------------------
-// (a1, from positions) cos/sin tables of a 3-axis token grid  [ERNIE-fuse §1]
+// Cos/sin tables of a 3-axis token grid  [ERNIE-fuse §1]
 //
 // Token s of a (T, Hg, Wg) grid sits at (t, h, w), s = (t*Hg + h)*Wg + w,
 // with t shifted by the batch row's offset.  Half-column c of axis k (local
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_grid_kernel(CosSinGridPa
 }
 
 // ---------------------------------------------------------------------------
-// (a2, a3) rotate-half RoPE with tail passthrough     [ERNIE-fuse §2]
+// Rotate-half RoPE with tail passthrough     [ERNIE-fuse §2]
 //
 // A workgroup owns one view and tok_per_wg consecutive tokens (table rows
 // t0 ...); the views of the same tokens sit in neighbouring workgroups so
@@ -682,7 +682,7 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
 #endif
 
 // ---------------------------------------------------------------------------
-// (a4, a5) GEGLU with activation rounding             [ERNIE-fuse §3]
+// GEGLU with activation rounding             [ERNIE-fuse §3]
 //
 // G(x) = rne_bf16(x * Phi(x)) takes one of 65536 inputs, so it is tabulated
 // where it is not a simple function of the bits:
@@ -846,7 +846,7 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
 }
 
 // ---------------------------------------------------------------------------
-// (f3) GEGLU as the epilogue of the gate_up projection      [ERNIE-fuse §3]
+// GEGLU as the epilogue of the gate_up projection      [ERNIE-fuse §3]
 //
 // out = x W^T on the matrix cores (v_mfma_f32_32x32x16_bf16, fp32
 // accumulation), the eager bf16 rounding of the projection applied to each

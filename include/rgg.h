@@ -64,7 +64,7 @@ typedef enum rgg_status {
 } rgg_status;
 
 /*
- * (a1) Hoisted rotary tables.                              [ERNIE-fuse §1]
+ * Hoisted rotary tables.                              [ERNIE-fuse §1]
  *
  * The rotary angles `freqs` have the page's shape (S, B, 1, R) in fp32: the
  * angle of sequence position s, batch row b, rotary column j is
@@ -87,7 +87,7 @@ RGG_API int rope_cossin_precompute(const float *freqs, int64_t S, int64_t B, int
                            uint16_t *cos_out, uint16_t *sin_out, hipStream_t stream);
 
 /*
- * (a1, from positions) Rotary tables straight from a 3-axis token grid.
+ * Rotary tables straight from a 3-axis token grid.
  *                            [ERNIE-fuse §1, the angles the table hoist is fed]
  *
  * The same tables as rope_cossin_precompute, for the angles a 3-axis
@@ -130,7 +130,7 @@ typedef struct rgg_rope_view {
 } rgg_rope_view;
 
 /*
- * (a2, a3) Rotate-half RoPE with tail passthrough.          [ERNIE-fuse §2]
+ * Rotate-half RoPE with tail passthrough.          [ERNIE-fuse §2]
  *
  * For every view v, token (b, s), head h, with c and sn the bf16 rows
  * b*S + s of `cos` and `sin` (contiguous (B*S, R)) and h2 = R/2:
@@ -161,7 +161,7 @@ RGG_API int rope_rotate_half_bf16(const rgg_rope_view *views, int n_views, int64
                           const uint16_t *sin, hipStream_t stream);
 
 /*
- * (a4, a5) GEGLU with activation rounding.                  [ERNIE-fuse §3]
+ * GEGLU with activation rounding.                  [ERNIE-fuse §3]
  *
  * `input` is (rows, 2*hidden) bf16 with row stride in_row_stride: the first
  * `hidden` columns are the gate, the next `hidden` the up projection.  Writes
@@ -186,7 +186,7 @@ RGG_API int gelu_and_mul_bf16(const uint16_t *input, int64_t rows, int64_t hidde
                       hipStream_t stream);
 
 /*
- * (f3) The gate_up projection, alone or with GEGLU fused into its epilogue.
+ * The gate_up projection, alone or with GEGLU fused into its epilogue.
  *                                   [ERNIE-fuse §3, the projection before it]
  *
  * x is (M, K) bf16 with row stride x_stride; W is a linear layer's weight

@@ -80,7 +80,7 @@ class Oracle:
         """rne_bf16(GELU(x)) for all 65536 bf16 bit patterns x."""
         return np.array([self.lib.oracle_gelu_bf16(i) for i in range(65536)], dtype=np.uint16)
 
-    # -- (a1) cos/sin tables -------------------------------------------------
+    # -- Cos/sin tables -------------------------------------------------
     def rope_cossin(self, freqs):
         """freqs: float32 (S, B, 1, R) array (any strides with unit last stride).
 
@@ -120,7 +120,7 @@ class Oracle:
         """The (B*S, R) cos/sin tables of the grid's angles."""
         return self.rope_cossin(self.rope_angles_grid(B, grid, dims, theta, t_offset))
 
-    # -- (f3) gate_up projection and GEGLU on it -----------------------------
+    # -- Gate_up projection and GEGLU on it -----------------------------
     def gemm_bf16(self, x, w):
         """x: uint16 (M, K), w: uint16 (N, K).  Returns rne_bf16(x w^T), (M, N)."""
         x = np.ascontiguousarray(x, dtype=np.uint16)
@@ -144,7 +144,7 @@ class Oracle:
         assert rc == 0
         return out
 
-    # -- (a2, a3) rotate-half ------------------------------------------------
+    # -- Rotate-half ------------------------------------------------
     def rope_rotate_half(self, x, cos, sin):
         """x: uint16 (B, S, H, D); cos/sin: uint16 (B*S, R).  Returns out (B, S, H, D)."""
         x = np.ascontiguousarray(x, dtype=np.uint16)
@@ -187,7 +187,7 @@ class Oracle:
                                                _ptr(sin, _f64p), _ptr(out, _f64p))
         return out
 
-    # -- (a4, a5) GEGLU ------------------------------------------------------
+    # -- GEGLU ------------------------------------------------------
     def gelu_and_mul(self, inp):
         """inp: uint16 (rows, 2*hidden), gate first then up.  Returns (rows, hidden)."""
         inp = np.ascontiguousarray(inp, dtype=np.uint16)

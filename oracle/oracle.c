@@ -129,7 +129,7 @@ static double keep_exact(double v)
 }
 
 /* ---------------------------------------------------------------------------
- * (a1) hoisted cos/sin tables          [ERNIE-fuse §1]
+ * Hoisted cos/sin tables          [ERNIE-fuse §1]
  *
  * freqs has shape (S, B, 1, R): the angle for sequence position s, batch row
  * b, rotary column j is at freqs[s*stride_s + b*stride_b + j].  The page
@@ -154,7 +154,7 @@ ORACLE_API void oracle_rope_cossin(const float *freqs, int64_t S, int64_t B, int
 }
 
 /* ---------------------------------------------------------------------------
- * (f2) rotary angles of a 3-axis token grid       [ERNIE-fuse §1, the angles
+ * Rotary angles of a 3-axis token grid       [ERNIE-fuse §1, the angles
  *                                                  the table hoist is fed]
  *
  * The page hoists the tables from angles that the model's 3-axis positional
@@ -197,7 +197,7 @@ ORACLE_API void oracle_rope_angles_grid(int64_t B, int64_t T, int64_t Hg, int64_
 }
 
 /* ---------------------------------------------------------------------------
- * (a2, a3) rotate-half RoPE with tail passthrough   [ERNIE-fuse §2]
+ * Rotate-half RoPE with tail passthrough   [ERNIE-fuse §2]
  *
  * The page's eager chain splits the leading R columns into two halves of
  * width h = R/2, forms the rotate-half partner (the negated second half
@@ -306,7 +306,7 @@ ORACLE_API void oracle_rope_rotate_half_exact(const double *x, int64_t B, int64_
 }
 
 /* ---------------------------------------------------------------------------
- * (a4, a5) GEGLU with activation rounding          [ERNIE-fuse §3]
+ * GEGLU with activation rounding          [ERNIE-fuse §3]
  *
  * The eager form is up * F.gelu(gate) on bf16 tensors: F.gelu's default is
  * the exact (erf) GELU, GELU(x) = x * Phi(x), Phi(x) = erfc(-x / sqrt 2) / 2,
@@ -371,7 +371,7 @@ ORACLE_API void oracle_gelu_and_mul(const uint16_t *input, int64_t rows, int64_t
 }
 
 /* ---------------------------------------------------------------------------
- * (f3) the gate_up projection feeding GEGLU, and GEGLU on its output
+ * The gate_up projection feeding GEGLU, and GEGLU on its output
  *                                   [ERNIE-fuse §3, the projection before it]
  *
  * The page's GEGLU input is the output of the FFN's gate_up linear layer,

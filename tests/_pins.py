@@ -98,7 +98,7 @@ def check_rounding_vs_torch(o):
 
 
 # ---------------------------------------------------------------------------
-# (a2, a3) rotate-half
+# Rotate-half
 # ---------------------------------------------------------------------------
 
 def check_rope_worked_vectors(o):
@@ -215,7 +215,7 @@ def check_rope_rows_form(o):
 
 
 # ---------------------------------------------------------------------------
-# (a1) cos/sin tables
+# Cos/sin tables
 # ---------------------------------------------------------------------------
 
 def _check_table_vs_mpmath(freq_values, cos_bits, sin_bits):
@@ -260,7 +260,7 @@ def check_cossin_row_order(o):
 
 
 # ---------------------------------------------------------------------------
-# (f2) rotary angles of a 3-axis token grid
+# Rotary angles of a 3-axis token grid
 # ---------------------------------------------------------------------------
 
 GRID_CASES = [  # B, grid, dims, theta, t_offset
@@ -311,7 +311,7 @@ def check_angles_grid_closed_forms(o):
 
 
 # ---------------------------------------------------------------------------
-# (a4, a5) GELU and the multiply
+# GELU and the multiply
 # ---------------------------------------------------------------------------
 
 def check_gelu_closed_forms(o):
@@ -393,7 +393,7 @@ def check_mul_rounding_vs_torch(o):
 
 
 # ---------------------------------------------------------------------------
-# (f3) the gate_up projection and GEGLU on it
+# The gate_up projection and GEGLU on it
 # ---------------------------------------------------------------------------
 
 def _finite_bits(a):

@@ -68,7 +68,7 @@ def with_guards(shape, fill=0x7FC1):
 
 
 # ---------------------------------------------------------------------------
-# (a1) cos/sin tables
+# Cos/sin tables
 # ---------------------------------------------------------------------------
 
 def gpu_cossin(freqs_np):
@@ -145,7 +145,7 @@ def test_cossin_empty_and_guards(orc):
 
 
 # ---------------------------------------------------------------------------
-# (a1, from positions) cos/sin tables of a 3-axis token grid
+# Cos/sin tables of a 3-axis token grid
 # ---------------------------------------------------------------------------
 
 GRID_TABLES = [  # B, grid, dims, theta, t_offset
@@ -192,7 +192,7 @@ def test_cossin_from_grid_empty():
 
 
 # ---------------------------------------------------------------------------
-# (a2, a3) rotate-half RoPE
+# Rotate-half RoPE
 # ---------------------------------------------------------------------------
 
 def oracle_rope(orc, x, cos, sin):
@@ -483,7 +483,7 @@ def test_rope_dit_layer_full_size(orc):
 
 
 # ---------------------------------------------------------------------------
-# (a4, a5) GEGLU
+# GEGLU
 # ---------------------------------------------------------------------------
 
 def test_gelu_all_65536_inputs(orc):
@@ -639,7 +639,7 @@ def test_geglu_full_size(orc, wid):
 
 
 # ---------------------------------------------------------------------------
-# (f3) the gate_up projection, alone and with GEGLU in its epilogue
+# The gate_up projection, alone and with GEGLU in its epilogue
 #
 # Bars: on exact-sum inputs (small integers times 2^-4: every partial sum is
 # exact in fp32, whatever the order) the projection and the fused GEGLU are
