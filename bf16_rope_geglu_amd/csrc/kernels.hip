@@ -1303,24 +1303,29 @@ hipError_t launch_gelu_and_mul(const GegluParams &p, int grid, hipStream_t strea
 
 hipError_t launch_gemm_gate_up(const GemmParams &p, bool geglu, hipStream_t stream)
 {
-    // The double-buffered tiles take 72 KiB of LDS, above the 64 KiB a launch
-    // gets without asking; the attribute is per kernel and process-wide.
-    static std::once_flag once;
-    static hipError_t attr = hipSuccess;
-    std::call_once(once, [] {
-        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_gate_up_kernel<true>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-        if (attr == hipSuccess)
-            attr = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_gate_up_kernel<false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-    });
-    if (attr != hipSuccess)
-        return attr;
-    // One workgroup per CU (the LDS use allows no more), each walking tiles.
+    // The four stages and the table take 135 KiB of LDS, above the 64 KiB a
+    // launch gets without asking.  The attribute is set once per device (it
+    // belongs to the kernel as loaded on the current device).
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static hipError_t attr[kMaxDevices];
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess)
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev] {
+        attr[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_gate_up_kernel<true>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+        if (attr[dev] == hipSuccess)
+            attr[dev] = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_gate_up_kernel<false>),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+    });
+    if (attr[dev] != hipSuccess)
+        return attr[dev];
+    // One workgroup per CU (the LDS use allows no more), each walking tiles.
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess)
         return e;
     const uint32_t tiles = p.mblocks * p.nblocks;

@@ -760,6 +760,55 @@ def test_gemm_zero_k_and_empty(orc):
     assert h0.shape == (3, 0)
 
 
+def test_gemm_side_stream_and_first_calls_from_threads(orc):
+    """In a fresh process, four host threads make their first projection
+    calls at once (the per-device kernel attribute and the GELU table are
+    set up once), each on its own stream; every result matches the oracle."""
+    import subprocess
+    import sys
+    import tempfile
+    code = r"""
+import sys, threading
+sys.path.insert(0, %r)
+import numpy as np
+import torch
+import bf16_rope_geglu_amd as rgg
+import workloads as W
+N = 4
+xs = [W.small_int_bf16((300 + 50 * k, 128), 9700 + k) for k in range(N)]
+ws = [W.small_int_bf16((256, 128), 9710 + k) for k in range(N)]
+dx = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in xs]
+dw = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in ws]
+outs = [None] * N
+streams = [torch.cuda.Stream() for _ in range(N)]
+torch.cuda.synchronize()
+go = threading.Barrier(N)
+def work(k):
+    with torch.cuda.stream(streams[k]):
+        go.wait()
+        outs[k] = rgg.gemm_geglu_bf16(dx[k], dw[k]) if k %% 2 == 0 else rgg.gemm_bf16_nt(dx[k], dw[k])
+threads = [threading.Thread(target=work, args=(k,)) for k in range(N)]
+for t in threads: t.start()
+for t in threads: t.join()
+torch.cuda.synchronize()
+for k in range(N):
+    np.save(sys.argv[1] + "/x%%d.npy" %% k, xs[k])
+    np.save(sys.argv[1] + "/w%%d.npy" %% k, ws[k])
+    np.save(sys.argv[1] + "/out%%d.npy" %% k, outs[k].view(torch.int16).cpu().numpy().view(np.uint16))
+print("ok", flush=True)
+""" % os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    say("gemm first calls from 4 threads (fresh process)")
+    with tempfile.TemporaryDirectory() as d:
+        r = subprocess.run([sys.executable, "-c", code, d], capture_output=True, text=True,
+                           timeout=110)
+        assert r.returncode == 0 and "ok" in r.stdout, r.stderr[-2000:]
+        for k in range(4):
+            x, w = np.load(f"{d}/x{k}.npy"), np.load(f"{d}/w{k}.npy")
+            got = np.load(f"{d}/out{k}.npy")
+            want = orc.gemm_geglu(x, w) if k % 2 == 0 else orc.gemm_bf16(x, w)
+            assert_bitexact(got, want, f"thread {k}")
+
+
 def test_gemm_full_size(orc):
     """The dit-layer projection at its full size, 32768 x 4096 times
     (2 x 8192) x 4096: exact-sum inputs bit-exact with the oracle on sampled
@@ -864,9 +913,10 @@ def test_geglu_wide_rows(orc):
 
 
 def test_graph_capture_replays(orc):
-    """All three entry points captured in one HIP graph and replayed several
-    times, with eager work and synchronisation between replays; every replay
-    matches the eager result."""
+    """The entry points captured in one HIP graph (tables, RoPE, GEGLU and the
+    projection with GEGLU fused) and replayed several times, with eager work
+    and synchronisation between replays; every replay matches the eager
+    result."""
     say("graph capture of the whole path")
     rgg.prepare_device(0)
     B, S, H, D, R = 1, 64, 4, 64, 64
@@ -877,25 +927,30 @@ def test_graph_capture_replays(orc):
     sin = torch.empty_like(cos)
     xo = torch.empty_like(x)
     go = torch.empty((96, 128), dtype=torch.bfloat16, device="cuda")
+    xg = dev(W.normal_bf16((300, 128), 8703))
+    wg = dev(W.normal_bf16((256, 128), 8704, 1.0 / np.sqrt(128)))
+    pg = torch.empty((300, 128), dtype=torch.bfloat16, device="cuda")
 
     def path():
         rgg.rope_cossin_precompute(fr, cos, sin)
         rgg.rope_rotate_half_bf16(x, cos, sin, out=xo)
         rgg.gelu_and_mul_bf16(inp, go)
+        rgg.gemm_geglu_bf16(xg, wg, pg)
 
+    outs = (cos, sin, xo, go, pg)
     path()
-    want = [host(t).copy() for t in (cos, sin, xo, go)]
+    want = [host(t).copy() for t in outs]
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         path()
     for rep in range(4):
-        for t in (cos, sin, xo, go):
+        for t in outs:
             t.zero_()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        got = [host(t) for t in (cos, sin, xo, go)]
-        for g, w, name in zip(got, want, ("cos", "sin", "rope", "geglu")):
+        got = [host(t) for t in outs]
+        for g, w, name in zip(got, want, ("cos", "sin", "rope", "geglu", "projection geglu")):
             assert np.array_equal(g, w), f"replay {rep}: {name} differs from eager"
         _ = (x.float() * 2).sum().item()  # eager work between replays
 
