@@ -971,7 +971,9 @@ void gemm_gate_up_kernel(GemmParams p)
     // would make every later LDS read wait for every load in flight; here
     // the ordering is explicit: "vmcnt" waits before each barrier, and a
     // stage is only reloaded after the barrier that ends its last reads.
-    // The instruction has no register result.
+    // The instruction has no register result, and nothing else in this
+    // kernel uses M0 (no other LDS-direct, message or relative-move
+    // instruction), so setting it here disturbs no compiler state.
     const uint32_t lds0 = (uint32_t)(uintptr_t)gsm + kGemmLutBytes + wv * 2 * 1024;
     auto dma1 = [&](int kt, int st, int idx) {
         const int j = idx & 1;
