@@ -202,9 +202,11 @@ RGG_API int gelu_and_mul_bf16(const uint16_t *input, int64_t rows, int64_t hidde
  *                       The (M, 2H) projection never goes to memory.
  * For the same x and W, gemm_geglu_bf16 returns bit for bit what
  * gelu_and_mul_bf16 returns on the output of gemm_bf16_nt (one accumulation
- * order serves both).  The fp32 accumulation order is the kernel's, so a
- * projection output can differ by one bf16 step from the exactly rounded sum
- * when that sum lies within the accumulation error of a rounding boundary.
+ * order serves both).  The fp32 accumulation order is the kernel's: a
+ * projection output is the bf16 rounding of a value within
+ * 2 (K + 16) 2^-24 sum_k |x[m][k] W[n][k]| of the exact sum, so it differs
+ * from the exactly rounded sum only where that error reaches across a
+ * rounding boundary (and never where every partial sum is exact in fp32).
  *
  * Requirements: M, K >= 0; K a multiple of 64; N a multiple of 128 (H a
  * multiple of 64); rows of x and W at least K long, output rows at least N
