@@ -331,7 +331,7 @@ int gemm_checks(const uint16_t *x, int64_t M, int64_t K, int64_t x_stride, const
         return RGG_ERR_ALIGN;
     const int64_t mblocks = (M + 255) / 256, nblocks = (H + 127) / 128;
     if (M >= kMax32 || K >= kMax32 || mblocks * nblocks >= ((int64_t)1 << 24) || H >= kMax32 / 2 ||
-        x_stride >= ((int64_t)1 << 23) || w_stride >= ((int64_t)1 << 23))
+        x_stride >= ((int64_t)1 << 22) || w_stride >= ((int64_t)1 << 22))
         return RGG_ERR_UNSUPPORTED;
     if (K > 0) {
         const int64_t xn[1] = {M}, xs[1] = {x_stride}, wn[1] = {2 * H}, ws[1] = {w_stride};

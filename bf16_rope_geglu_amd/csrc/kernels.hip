@@ -943,8 +943,8 @@ void gemm_gate_up_kernel(GemmParams p)
     // brings row 16g + i / 4, logical chunk (i % 4) ^ ((i / 16) % 4), to LDS
     // chunk i % 4 of that row.  The loads address memory as a wave-uniform
     // base (SGPRs) plus a per-lane 32-bit byte offset fixed for the tile;
-    // offsets stay below 256 row strides, so strides are limited to 2^23
-    // elements.  Rows past M re-read row M-1 and columns past H re-read
+    // offsets stay below 256 row strides; strides are limited to 2^22
+    // elements, which keeps every offset below 2^31.  Rows past M re-read row M-1 and columns past H re-read
     // column H-1 (not stored).  (The lane index passes through an empty asm
     // statement so that the compiler recomputes the offsets per tile instead
     // of keeping loop-invariant copies alive across the tile loop.)

@@ -212,7 +212,7 @@ RGG_API int gelu_and_mul_bf16(const uint16_t *input, int64_t rows, int64_t hidde
  * multiple of 64); rows of x and W at least K long, output rows at least N
  * (H) long; 16-byte aligned bases and strides that are multiples of 8; out
  * may not overlap x or W.  M or N (H) zero: no work; K zero: zeros (and G(0)).
- * Limits: M, K < 2^31, row strides of x and W < 2^23 elements and
+ * Limits: M, K < 2^31, row strides of x and W < 2^22 elements and
  * ceil(M/256) * ceil(H/128) < 2^24.  gemm_geglu_bf16 builds
  * the GELU table like gelu_and_mul_bf16 (RGG_ERR_CAPTURING applies).
  */

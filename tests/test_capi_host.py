@@ -196,8 +196,8 @@ def test_gemm_checks(lib, geglu):
     assert g(M=1 << 24, N=h * (1 if geglu else 2),
              os_=h * (1 if geglu else 2)) == UNSUPPORTED   # 2^16 x 2^8 = 2^24 blocks
     assert g(K=1 << 31, xs=1 << 31, ws=1 << 31) == UNSUPPORTED   # K >= 2^31
-    assert g(xs=1 << 23) == UNSUPPORTED                # x row stride >= 2^23
-    assert g(ws=1 << 23) == UNSUPPORTED                # W row stride >= 2^23
+    assert g(xs=1 << 22) == UNSUPPORTED                # x row stride >= 2^22
+    assert g(ws=1 << 22) == UNSUPPORTED                # W row stride >= 2^22
 
 
 def test_gemm_plain_needs_whole_gate_up_pairs(lib):

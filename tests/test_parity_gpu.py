@@ -760,6 +760,32 @@ def test_gemm_zero_k_and_empty(orc):
     assert h0.shape == (3, 0)
 
 
+def test_gemm_long_k_and_widest_strides(orc):
+    """Exact-sum inputs with K = 16384 (partial sums stay exact in fp32), and
+    x and W rows at the largest row stride the projection takes (2^22 - 8
+    elements: 256 rows of x span 2 GiB), bit-exact with the oracle."""
+    say("gemm K = 16384")
+    x = W.small_int_bf16((200, 16384), 9801)
+    w = W.small_int_bf16((128, 16384), 9802)
+    assert_bitexact(host(rgg.gemm_geglu_bf16(dev(x), dev(w))), orc.gemm_geglu(x, w), "K 16384 fused")
+    assert_bitexact(host(rgg.gemm_bf16_nt(dev(x), dev(w))), orc.gemm_bf16(x, w), "K 16384 plain")
+    stride = (1 << 22) - 8
+    say(f"gemm row stride {stride} (x 256 rows, W 256 rows)")
+    M, K, H = 256, 64, 128
+    xs = W.small_int_bf16((M, K), 9803)
+    ws = W.small_int_bf16((2 * H, K), 9804)
+    bx = torch.empty((M, stride), dtype=torch.bfloat16, device="cuda")
+    bw = torch.empty((2 * H, stride), dtype=torch.bfloat16, device="cuda")
+    bx[:, :K].copy_(dev(xs))
+    bw[:, :K].copy_(dev(ws))
+    got_f = host(rgg.gemm_geglu_bf16(bx[:, :K], bw[:, :K]))
+    got_p = host(rgg.gemm_bf16_nt(bx[:, :K], bw[:, :K]))
+    del bx, bw
+    torch.cuda.empty_cache()
+    assert_bitexact(got_f, orc.gemm_geglu(xs, ws), "widest strides fused")
+    assert_bitexact(got_p, orc.gemm_bf16(xs, ws), "widest strides plain")
+
+
 def test_gemm_side_stream_and_first_calls_from_threads(orc):
     """In a fresh process, four host threads make their first projection
     calls at once (the per-device kernel attribute and the GELU table are
