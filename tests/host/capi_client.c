@@ -1,17 +1,20 @@
 /*
  * A plain C client of include/rgg.h: no Python, no torch.  It reads one
  * workload from a binary file, runs the three entry points on the current
- * HIP device with device memory it allocates itself, and writes the results
+ * HIP device with device memory it allocates itself (and the gate_up
+ * projection, fused with GEGLU and alone), and writes the results
  * to another binary file, which tests/test_parity_gpu.py compares with the
  * CPU oracle.
  *
  * Input file, little-endian:
- *   int64 S, B, H, D, R, rows, hidden
+ *   int64 S, B, H, D, R, rows, hidden, M, K, Hp
  *   float freqs[S][B][R]                    (the (S, B, 1, R) angles)
  *   uint16 x[B][S][H][D]                    (bf16 bits)
  *   uint16 gate_up[rows][2 * hidden]        (bf16 bits)
+ *   uint16 px[M][K], pw[2 * Hp][K]          (the projection's input and weight)
  * Output file:
- *   uint16 cos[B*S][R], sin[B*S][R], rope[B][S][H][D], geglu[rows][hidden]
+ *   uint16 cos[B*S][R], sin[B*S][R], rope[B][S][H][D], geglu[rows][hidden],
+ *          fused[M][Hp] (gemm_geglu_bf16), proj[M][2 * Hp] (gemm_bf16_nt)
  *
  * Usage: capi_client IN OUT      (exit status 0 on success)
  */
@@ -55,25 +58,30 @@ int main(int argc, char **argv)
     FILE *in = fopen(argv[1], "rb");
     if (!in)
         return 1;
-    int64_t hdr[7];
+    int64_t hdr[10];
     if (!read_all(in, hdr, sizeof hdr))
         return 1;
     const int64_t S = hdr[0], B = hdr[1], H = hdr[2], D = hdr[3], R = hdr[4];
-    const int64_t rows = hdr[5], hidden = hdr[6];
+    const int64_t rows = hdr[5], hidden = hdr[6], M = hdr[7], K = hdr[8], Hp = hdr[9];
     const size_t n_f = (size_t)(S * B * R), n_x = (size_t)(B * S * H * D);
     const size_t n_t = (size_t)(B * S * R), n_g = (size_t)(rows * 2 * hidden);
     const size_t n_o = (size_t)(rows * hidden);
+    const size_t n_px = (size_t)(M * K), n_pw = (size_t)(2 * Hp * K);
+    const size_t n_pf = (size_t)(M * Hp), n_pp = (size_t)(M * 2 * Hp);
+    const size_t n_out = 2 * n_t + n_x + n_o + n_pf + n_pp;
 
     float *h_f = malloc(n_f * sizeof(float));
     uint16_t *h_x = malloc(n_x * 2), *h_g = malloc(n_g * 2);
-    uint16_t *h_out = malloc((2 * n_t + n_x + n_o) * 2);
-    if (!h_f || !h_x || !h_g || !h_out || !read_all(in, h_f, n_f * 4) ||
-        !read_all(in, h_x, n_x * 2) || !read_all(in, h_g, n_g * 2))
+    uint16_t *h_px = malloc(n_px * 2), *h_pw = malloc(n_pw * 2);
+    uint16_t *h_out = malloc(n_out * 2);
+    if (!h_f || !h_x || !h_g || !h_px || !h_pw || !h_out || !read_all(in, h_f, n_f * 4) ||
+        !read_all(in, h_x, n_x * 2) || !read_all(in, h_g, n_g * 2) ||
+        !read_all(in, h_px, n_px * 2) || !read_all(in, h_pw, n_pw * 2))
         return 1;
     fclose(in);
 
     float *d_f;
-    uint16_t *d_x, *d_g, *d_cos, *d_sin, *d_rope, *d_geglu;
+    uint16_t *d_x, *d_g, *d_cos, *d_sin, *d_rope, *d_geglu, *d_px, *d_pw, *d_pf, *d_pp;
     CHECK_HIP(hipMalloc((void **)&d_f, n_f * 4));
     CHECK_HIP(hipMalloc((void **)&d_x, n_x * 2));
     CHECK_HIP(hipMalloc((void **)&d_g, n_g * 2));
@@ -81,9 +89,15 @@ int main(int argc, char **argv)
     CHECK_HIP(hipMalloc((void **)&d_sin, n_t * 2));
     CHECK_HIP(hipMalloc((void **)&d_rope, n_x * 2));
     CHECK_HIP(hipMalloc((void **)&d_geglu, n_o * 2));
+    CHECK_HIP(hipMalloc((void **)&d_px, n_px * 2));
+    CHECK_HIP(hipMalloc((void **)&d_pw, n_pw * 2));
+    CHECK_HIP(hipMalloc((void **)&d_pf, n_pf * 2));
+    CHECK_HIP(hipMalloc((void **)&d_pp, n_pp * 2));
     CHECK_HIP(hipMemcpy(d_f, h_f, n_f * 4, hipMemcpyHostToDevice));
     CHECK_HIP(hipMemcpy(d_x, h_x, n_x * 2, hipMemcpyHostToDevice));
     CHECK_HIP(hipMemcpy(d_g, h_g, n_g * 2, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(d_px, h_px, n_px * 2, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(d_pw, h_pw, n_pw * 2, hipMemcpyHostToDevice));
 
     hipStream_t stream;
     CHECK_HIP(hipStreamCreateWithFlags(&stream, hipStreamNonBlocking));
@@ -96,14 +110,21 @@ int main(int argc, char **argv)
 
     CHECK_RGG(gelu_and_mul_bf16(d_g, rows, hidden, 2 * hidden, d_geglu, hidden, stream));
 
+    /* x (M, K) and W (2 Hp, K) contiguous; outputs (M, Hp) and (M, 2 Hp) */
+    CHECK_RGG(gemm_geglu_bf16(d_px, M, K, K, d_pw, Hp, K, d_pf, Hp, stream));
+    CHECK_RGG(gemm_bf16_nt(d_px, M, K, K, d_pw, 2 * Hp, K, d_pp, 2 * Hp, stream));
+
     CHECK_HIP(hipStreamSynchronize(stream));
     CHECK_HIP(hipMemcpy(h_out, d_cos, n_t * 2, hipMemcpyDeviceToHost));
     CHECK_HIP(hipMemcpy(h_out + n_t, d_sin, n_t * 2, hipMemcpyDeviceToHost));
     CHECK_HIP(hipMemcpy(h_out + 2 * n_t, d_rope, n_x * 2, hipMemcpyDeviceToHost));
     CHECK_HIP(hipMemcpy(h_out + 2 * n_t + n_x, d_geglu, n_o * 2, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(h_out + 2 * n_t + n_x + n_o, d_pf, n_pf * 2, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(h_out + 2 * n_t + n_x + n_o + n_pf, d_pp, n_pp * 2,
+                        hipMemcpyDeviceToHost));
 
     FILE *out = fopen(argv[2], "wb");
-    if (!out || fwrite(h_out, 2, 2 * n_t + n_x + n_o, out) != 2 * n_t + n_x + n_o)
+    if (!out || fwrite(h_out, 2, n_out, out) != n_out)
         return 1;
     fclose(out);
 
@@ -115,9 +136,15 @@ int main(int argc, char **argv)
     hipFree(d_sin);
     hipFree(d_rope);
     hipFree(d_geglu);
+    hipFree(d_px);
+    hipFree(d_pw);
+    hipFree(d_pf);
+    hipFree(d_pp);
     free(h_f);
     free(h_x);
     free(h_g);
+    free(h_px);
+    free(h_pw);
     free(h_out);
     printf("capi_client: ok\n");
     return 0;

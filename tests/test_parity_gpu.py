@@ -1097,29 +1097,40 @@ def test_plain_c_client(orc, tmp_path):
 
     assert os.path.exists(CLIENT), "tests/host/_bin/capi_client is not built"
     S, B, H, D, R, rows, hidden = 300, 2, 3, 64, 48, 77, 136
-    say(f"C client: rope ({B},{S},{H},{D}) R={R}, geglu ({rows},{hidden})")
+    M, K, Hp = 333, 192, 192
+    say(f"C client: rope ({B},{S},{H},{D}) R={R}, geglu ({rows},{hidden}), "
+        f"projection ({M},{K}) x (2*{Hp},{K})")
     freqs = W.freqs_unpaired(S, B, R, 71)
     x = W.normal_bf16((B, S, H, D), 72)
     inp = np.concatenate([W.normal_bf16((rows, hidden), 73, 2.0),
                           W.normal_bf16((rows, hidden), 74)], axis=1)
+    px = W.small_int_bf16((M, K), 75)
+    pw = W.small_int_bf16((2 * Hp, K), 76)
     src, dst = tmp_path / "in.bin", tmp_path / "out.bin"
     with open(src, "wb") as f:
-        f.write(np.array([S, B, H, D, R, rows, hidden], np.int64).tobytes())
+        f.write(np.array([S, B, H, D, R, rows, hidden, M, K, Hp], np.int64).tobytes())
         f.write(np.ascontiguousarray(freqs, np.float32).tobytes())
         f.write(np.ascontiguousarray(x, np.uint16).tobytes())
         f.write(np.ascontiguousarray(inp, np.uint16).tobytes())
+        f.write(np.ascontiguousarray(px, np.uint16).tobytes())
+        f.write(np.ascontiguousarray(pw, np.uint16).tobytes())
     proc = subprocess.run([CLIENT, str(src), str(dst)], capture_output=True, text=True,
                           timeout=60)
     say(proc.stdout.strip(), proc.stderr.strip())
     assert proc.returncode == 0, f"capi_client exit status {proc.returncode}"
     got = np.fromfile(dst, np.uint16)
     n_t, n_x = B * S * R, x.size
-    assert got.size == 2 * n_t + n_x + rows * hidden
+    n_o = rows * hidden
+    assert got.size == 2 * n_t + n_x + n_o + M * Hp + M * 2 * Hp
     cos, sin = got[:n_t].reshape(B * S, R), got[n_t:2 * n_t].reshape(B * S, R)
     rope = got[2 * n_t:2 * n_t + n_x].reshape(x.shape)
-    geglu = got[2 * n_t + n_x:].reshape(rows, hidden)
+    geglu = got[2 * n_t + n_x:2 * n_t + n_x + n_o].reshape(rows, hidden)
+    fused = got[2 * n_t + n_x + n_o:2 * n_t + n_x + n_o + M * Hp].reshape(M, Hp)
+    proj = got[2 * n_t + n_x + n_o + M * Hp:].reshape(M, 2 * Hp)
     oc, os_ = orc.rope_cossin(freqs)
     assert_ulp_bar(cos, oc, "C client cos")
     assert_ulp_bar(sin, os_, "C client sin")
     assert_bitexact(rope, oracle_rope(orc, x, cos, sin), "C client rope")
     assert_ulp_bar(geglu, orc.gelu_and_mul(inp), "C client geglu")
+    assert_bitexact(fused, orc.gemm_geglu(px, pw), "C client projection + GEGLU")
+    assert_bitexact(proj, orc.gemm_bf16(px, pw), "C client projection")
