@@ -244,6 +244,24 @@ def test_binding_rejects_host_tensors():
     tab = torch.zeros(2 * 16, 16, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         rgg.rope_cossin_from_grid(2, (1, 4, 4), (4, 6, 6), cos_out=tab, sin_out=tab.clone())
+    xp = torch.zeros(8, 64, dtype=torch.bfloat16)
+    wp = torch.zeros(128, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        rgg.gemm_geglu_bf16(xp, wp)
+    with pytest.raises(TypeError):
+        rgg.gemm_bf16_nt(xp, wp)
+
+
+def test_binding_projection_shape_checks():
+    """Shape errors are raised before anything reaches the library (or a
+    device): weight not (N, K) with the input's K, an odd gate/up row count."""
+    xp = torch.zeros(8, 64, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        rgg.gemm_geglu_bf16(xp, torch.zeros(128, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        rgg.gemm_geglu_bf16(xp, torch.zeros(129, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        rgg.gemm_bf16_nt(xp, torch.zeros(128, 64, 1, dtype=torch.bfloat16))
 
 
 def test_binding_error_carries_status(lib):
