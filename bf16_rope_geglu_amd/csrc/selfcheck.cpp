@@ -33,7 +33,16 @@ constexpr size_t kGe1In = 4096;       // GEGLU (256, 2*256): gate = every bf16 p
 constexpr size_t kGe1Out = kGe1In + 256 * 512 * 2;
 constexpr size_t kGe2In = kGe1Out + 256 * 256 * 2;   // same gates, up = 2
 constexpr size_t kGe2Out = kGe2In + 256 * 512 * 2;
-constexpr size_t kUsed = kGe2Out + 256 * 256 * 2;
+// bit 6: the projection, fused and plain: x (40, 64) one-hot rows
+// (x[m][k] = 1 for k = m), W (128, 64); out[m][n] = W[n][m] exactly.
+constexpr int kPm = 40, kPk = 64, kPh = 64;
+constexpr size_t kPx = kGe2Out + 256 * 256 * 2;
+constexpr size_t kPw = kPx + kPm * kPk * 2;
+constexpr size_t kPfOut = kPw + 2 * kPh * kPk * 2;
+constexpr size_t kPpOut = kPfOut + kPm * kPh * 2;
+constexpr size_t kUsed = kPpOut + kPm * 2 * kPh * 2;
+static_assert(kPx % 256 == 0 && kPw % 256 == 0 && kPfOut % 256 == 0 && kPpOut % 256 == 0,
+              "projection operands 256-byte aligned");
 static_assert(kUsed <= RGG_SELFCHECK_WORKSPACE_BYTES, "workspace layout");
 
 // bit 0: cos/sin of fp32 angles, correctly rounded (50-digit evaluation).
@@ -86,6 +95,11 @@ const uint16_t kGelu[8][2] = {
     {0xC040, 0xBB85},  // x = -3:  -0.0040496940, step 2^-15: 132.70 -> 133
     {0xC0B0, 0xB3E0},  // x = -5.5: -1.044426e-7, step 2^-31: 224.29 -> 224
 };
+
+// Gate and up of output (m, j) of the projection check: a textbook point of
+// the GELU table above and up = 1 or 2, so rne(up * G) is G or 2G exactly.
+uint16_t proj_gate(int m, int j) { return kGelu[(m + j) % 8][0]; }
+uint16_t proj_up(int m, int j) { return (m + j) % 2 ? 0x4000 : 0x3F80; }
 
 float bf16_value(uint16_t b)
 {
@@ -172,6 +186,14 @@ extern "C" int rgg_selfcheck(void *workspace, int64_t workspace_bytes, hipStream
         put<uint16_t>(in, kGe2In, r * 512 + 256 + c, 0x4000);  // up = 2
     }
 
+    for (int m = 0; m < kPm; ++m)
+        put<uint16_t>(in, kPx, (size_t)m * kPk + m, 0x3F80);
+    for (int j = 0; j < kPh; ++j)
+        for (int m = 0; m < kPm; ++m) {
+            put<uint16_t>(in, kPw, (size_t)j * kPk + m, proj_gate(m, j));
+            put<uint16_t>(in, kPw, (size_t)(kPh + j) * kPk + m, proj_up(m, j));
+        }
+
     if (hipMemcpyAsync(ws, in.data(), kUsed, hipMemcpyHostToDevice, stream) != hipSuccess)
         return RGG_ERR_HIP;
     int st = rope_cossin_precompute(reinterpret_cast<const float *>(ws + kFreq), 1, 1, 8, 8, 8,
@@ -195,6 +217,14 @@ extern "C" int rgg_selfcheck(void *workspace, int64_t workspace_bytes, hipStream
     if (st == RGG_OK)
         st = gelu_and_mul_bf16(reinterpret_cast<const uint16_t *>(ws + kGe2In), 256, 256, 512,
                                reinterpret_cast<uint16_t *>(ws + kGe2Out), 256, stream);
+    if (st == RGG_OK)
+        st = gemm_geglu_bf16(reinterpret_cast<const uint16_t *>(ws + kPx), kPm, kPk, kPk,
+                             reinterpret_cast<const uint16_t *>(ws + kPw), kPh, kPk,
+                             reinterpret_cast<uint16_t *>(ws + kPfOut), kPh, stream);
+    if (st == RGG_OK)
+        st = gemm_bf16_nt(reinterpret_cast<const uint16_t *>(ws + kPx), kPm, kPk, kPk,
+                          reinterpret_cast<const uint16_t *>(ws + kPw), 2 * kPh, kPk,
+                          reinterpret_cast<uint16_t *>(ws + kPpOut), 2 * kPh, stream);
     if (st != RGG_OK) {
         (void)hipStreamSynchronize(stream);
         return st;
@@ -267,6 +297,21 @@ extern "C" int rgg_selfcheck(void *workspace, int64_t workspace_bytes, hipStream
         if (!is_nan(G) && (G & 0x7FFFu) < 0x7F00u && g2(g) != bf16_bits(2.0f * gv))
             mask |= 1u << 5;
     }
+    // bit 6: the plain projection copies W's column m into row m; the fused
+    // output is G(gate) for up = 1 and 2 G(gate) for up = 2, both exact.
+    for (int m = 0; m < kPm; ++m)
+        for (int j = 0; j < kPh; ++j) {
+            const uint16_t gate = proj_gate(m, j), up = proj_up(m, j);
+            uint16_t G = 0;
+            for (int k = 0; k < 8; ++k)
+                if (kGelu[k][0] == gate)
+                    G = kGelu[k][1];
+            const uint16_t want = up == 0x4000 ? bf16_bits(2.0f * bf16_value(G)) : G;
+            if (get<uint16_t>(out, kPfOut, (size_t)m * kPh + j) != want ||
+                get<uint16_t>(out, kPpOut, (size_t)m * 2 * kPh + j) != gate ||
+                get<uint16_t>(out, kPpOut, (size_t)m * 2 * kPh + kPh + j) != up)
+                mask |= 1u << 6;
+        }
     if (failed)
         *failed = mask;
     return mask ? RGG_ERR_SELFCHECK : RGG_OK;

@@ -252,7 +252,10 @@ RGG_API int rgg_prepare_device(int device);
  *          the tabulated range (G = x for x >= 16, -0 for x <= -16, x/2 for
  *          2^-125 <= |x| < 2^-10, signed zeros, Inf and NaN) and its
  *          monotonicity for x > 0;
- *   bit 5  the multiply: up = 2 doubles every finite G below 2^127 exactly.
+ *   bit 5  the multiply: up = 2 doubles every finite G below 2^127 exactly;
+ *   bit 6  the projection on one-hot rows of x (out[m][n] = W[n][m] exactly,
+ *          plain), and with GEGLU fused where each gate is one of the points
+ *          of bit 3 and each up is 1 or 2 (out = G or 2 G exactly).
  * `*failed` (if not NULL) receives the mask of failed checks.  Returns
  * RGG_OK when every check passes, RGG_ERR_SELFCHECK otherwise.  Synchronous:
  * waits for `stream`.  Not allowed while `stream` is capturing

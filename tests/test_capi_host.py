@@ -344,6 +344,23 @@ def test_selfcheck_expected_values_agree_with_oracle_and_mpmath():
     gel = np.array(_c_array(text, "kGelu"), np.uint16).reshape(8, 2)
     for g, want in gel:
         assert o.gelu_bf16(int(g)) == want
+    # bit 6: one-hot x and W built as selfcheck.cpp describes; the oracle's
+    # projection copies W's column, and its fused GEGLU gives G or 2 G
+    M, K, H = 40, 64, 64
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), np.arange(M)] = 0x3F80
+    w = np.zeros((2 * H, K), np.uint16)
+    for j in range(H):
+        for m in range(M):
+            w[j, m] = gel[(m + j) % 8, 0]
+            w[H + j, m] = 0x4000 if (m + j) % 2 else 0x3F80
+    assert np.array_equal(o.gemm_bf16(x, w), w[:, :M].T)
+    fused = o.gemm_geglu(x, w)
+    for m in range(M):
+        for j in range(H):
+            G = float(np.array([int(gel[(m + j) % 8, 1]) << 16], np.uint32).view(np.float32)[0])
+            want = np.array([G * (2.0 if (m + j) % 2 else 1.0)], np.float32).view(np.uint32)[0] >> 16
+            assert fused[m, j] == want
 
 
 def test_cpu_baseline_leg_runs_on_a_small_sample():
