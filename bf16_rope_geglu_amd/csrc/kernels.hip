@@ -4,11 +4,12 @@
 // 통한 성능 최적화" (blog.secrett2633.cloud, analysis of sglang PR 34306),
 // cited as [ERNIE-fuse] with its section.
 //
-// Every kernel here is HBM-bound elementwise work: no matrix cores.  They move
-// data in 16-byte (8 x bf16) vectors per lane so that a wave64 load or store
-// covers whole cache lines, run 256-thread workgroups (four wave64s), and
-// round every eager bf16 op with the hardware's round-to-nearest-even
-// v_cvt_pk_bf16_f32.  IEEE fp32 subnormals are kept (the default denormal
+// The kernels of the path are HBM-bound elementwise work with no matrix
+// cores: they move data in 16-byte (8 x bf16) vectors per lane so that a
+// wave64 load or store covers whole cache lines, and round every eager bf16 op
+// with the hardware's round-to-nearest-even v_cvt_pk_bf16_f32.  The gate_up
+// projection at the end of the file is a contraction and runs on the matrix
+// cores (MFMA).  IEEE fp32 subnormals are kept (the default denormal
 // mode of gfx950 code objects) and nothing is contracted into an FMA across a
 // rounding point (the bf16 rounding sits between every multiply and add, and
 // the file is built with -ffp-contract=off).
@@ -862,9 +863,11 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
 // the second, so in a 32x32 block lane l holds output row l % 32 and, in its
 // accumulators v, output columns (v / 4) * 8 + (l / 32) * 4 + v % 4.
 // Operands: lane l supplies row l % 32 of W or of x and the 8 consecutive k
-// at (l / 32) * 8.  Two waves per SIMD matter here: a wave that issues a
-// global load waits until the CU's address unit takes it, and the other
-// wave on the SIMD keeps the matrix pipe busy meanwhile.
+// at (l / 32) * 8.  The two waves on a SIMD (one of rows 0-127, one of rows
+// 128-255) take turns: while one issues its 16 products on fragments already
+// in registers, the other reads the next slice's fragments and issues its
+// loads, so memory instructions never sit between a wave's products (a wave
+// that issues a global load waits until the CU's address unit takes it).
 //
 // Staging uses the direct global-to-LDS load (16 bytes per lane, one 1 KiB
 // run of LDS per instruction: 16 rows of 64 bytes), so the slices never pass
@@ -873,11 +876,12 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
 // from 64 four-byte banks; in an operand fetch those lanes read 16
 // consecutive rows at one logical chunk, and the swizzle puts them on 16
 // disjoint 16-byte bank groups (row r starts at group 4 (r % 4)).  Four
-// stages: the loads of slice kt + 3 are issued while slice kt is
-// multiplied, so a load has three slices of products to arrive (the first
-// touch of a line goes to HBM).  Before the barrier that ends slice kt, each
-// wave waits only for its own loads of slice kt + 1 (loads complete in
-// order).
+// stages: a wave issues its loads of slice kt + 3 right after reading its
+// fragments of slice kt, so a load has about three slices of products to
+// arrive (the first touch of a line goes to HBM).  A barrier ends every
+// half-turn; before the one after which slice kt + 1 is first read, each
+// wave waits only for its own loads of that slice (loads complete in order),
+// and a stage is reloaded only after both groups have read it.
 //
 // The workgroups are persistent (one per CU) and walk the tiles; the block
 // order is remapped so that each XCD (workgroups go to the 8 XCDs round
@@ -991,8 +995,8 @@ void gemm_gate_up_kernel(GemmParams p)
 
     f32x16 acc[4][2];  // [x row block][gate, up]
 
-    // Operand fragments, double buffered in registers (set 0 / set 1):
-    // 4 of x, then the gate and the up fragment of W.
+    // Operand fragments of one slice: set 0 for k 0-15, set 1 for k 16-31;
+    // each 4 of x, then the gate and the up fragment of W.
     const int ra = (wm * 128 + (lane & 31)) * 64;
     const int rb = (wn * 32 + (lane & 31)) * 64;
     bf16x8 fa[2][4], fb[2][2];
@@ -1035,62 +1039,77 @@ void gemm_gate_up_kernel(GemmParams p)
                 for (int v = 0; v < 16; ++v)
                     acc[a][b][v] = 0.0f;
 
-        // Each wave issues 4 loads per slice.  Instruction order inside a
-        // slice (fixed by scheduling fences): products 0-7 (set 0) carry the
-        // 6 fragment reads of set 1 and 2 loads of slice kt + 3; products
-        // 8-11 (set 1) carry the other 2 loads; then the wave waits for its
-        // loads of slice kt + 1 ("vmcnt(8)": slices kt + 2 and kt + 3 may
-        // still be in flight; loads complete in order) and passes the
-        // barrier; products 12-15 carry the 6 fragment reads of the next
-        // slice's set 0.
-        if (KT > 0) {
+        // Turns: waves 0-3 (group A, rows 0-127) and 4-7 (group B, rows
+        // 128-255) share the SIMDs pairwise and alternate between a compute
+        // half-turn (16 products on fragments already in registers) and a
+        // memory half-turn (the 12 fragment reads of slice s and the 4 loads
+        // of slice s + 3), so a SIMD's matrix pipe always has one wave
+        // feeding it.  A reads slice s + 1 while B multiplies slice s, and
+        // B reads slice s while A multiplies it.  Past the last slice the
+        // loads repeat slice KT - 1 into the stage that already holds it or
+        // into one both groups have finished reading (no branch in the loop).
+        const bool grpA = wv < 4;
+        auto memory = [&](int s_) {
+            if (s_ < KT) {
 #pragma unroll
-            for (int idx = 0; idx < 6; ++idx)
-                frag1(0, 0, 0, idx);
-            RGG_FENCE();
-            for (int kt = 0; kt + 1 < KT; ++kt) {
-                const int st = kt & 3;
-                const int kn = min(kt + 3, KT - 1), sn = (kt + 3) & 3;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    mma1(0, k);
-                    if (k < 6)
-                        frag1(st, 1, 1, k);
-                    if (k == 2 || k == 6)
-                        dma1(kn, sn, k >> 2);
-                    RGG_FENCE();
-                }
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    mma1(1, k);
-                    if (k == 0 || k == 2)
-                        dma1(kn, sn, 2 + (k >> 1));
-                    RGG_FENCE();
-                }
-                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-                __builtin_amdgcn_s_barrier();
-                RGG_FENCE();
-#pragma unroll
-                for (int k = 4; k < 8; ++k) {
-                    if (k < 7) {
-                        frag1((kt + 1) & 3, 0, 0, 2 * (k - 4));
-                        frag1((kt + 1) & 3, 0, 0, 2 * (k - 4) + 1);
-                    }
-                    mma1(1, k);
-                    RGG_FENCE();
+                for (int idx = 0; idx < 6; ++idx) {
+                    frag1(s_ & 3, 0, 0, idx);
+                    frag1(s_ & 3, 1, 1, idx);
                 }
             }
-            const int st = (KT - 1) & 3;
+            const int kn = min(s_ + 3, KT - 1), sn = (s_ + 3) & 3;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int idx = 0; idx < 4; ++idx)
+                dma1(kn, sn, idx);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        };
+        auto compute = [&]() {
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
                 mma1(0, k);
-                if (k < 6)
-                    frag1(st, 1, 1, k);
-                RGG_FENCE();
-            }
 #pragma unroll
             for (int k = 0; k < 8; ++k)
                 mma1(1, k);
+            __builtin_amdgcn_s_setprio(0);
+        };
+        if (KT > 0) {
+            // before the first turn: A reads slice 0 and loads slice 3
+            if (grpA) {
+                memory(0);
+                asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            }
+            __builtin_amdgcn_s_barrier();
+            RGG_FENCE();
+            if (grpA) {
+                for (int s_ = 0; s_ < KT; ++s_) {
+                    compute();                      // A multiplies slice s_
+                    RGG_FENCE();
+                    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    RGG_FENCE();
+                    memory(s_ + 1);                 // A reads slice s_ + 1
+                    RGG_FENCE();
+                    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    RGG_FENCE();
+                }
+            } else {
+                for (int s_ = 0; s_ < KT; ++s_) {
+                    memory(s_);                     // B reads slice s_
+                    RGG_FENCE();
+                    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    RGG_FENCE();
+                    compute();                      // B multiplies slice s_
+                    RGG_FENCE();
+                    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    RGG_FENCE();
+                }
+            }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();  // every wave is done with the operand stages
