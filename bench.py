@@ -376,6 +376,61 @@ def run_sweep(reps=40, touch=2 << 30):
                              stream_us(algo["geglu"], 2)))
         torch.cuda.empty_cache()
 
+    # One rank's share of dit_layer when the layer is split over 8 GPUs: the
+    # path has no exchange of its own, so a rank runs the same kernels on a
+    # slice, tokens (sequence parallel: qkv rows S/8, table rows of its own
+    # tokens; GEGLU rows/8) or heads (q and k with H/8 heads after the
+    # all-to-all, the whole table; GEGLU with hidden/8 columns).
+    P = 8
+    r = W.WORKLOADS[4]["rope"]
+    g = W.WORKLOADS[4]["geglu"]
+    B, S, H, D, R = r["B"], r["S"], r["H"], r["D"], r["R"]
+    fr_all = torch.from_numpy(W.workload_freqs(4)).to(dev)
+    for split, s_loc, h_loc in (("S/8 tokens", S // P, H), ("H/8 heads", S, H // P)):
+        label = f"dit_layer, 1 of {P} ranks ({split})"
+        T = B * s_loc
+        pre_b = T * R * 4 + 2 * T * R * 2
+        rope_b = 2 * (2 * T * h_loc * D * 2) + 2 * T * R * 2
+        nsets = max(2, -(-touch // (rope_b + pre_b)))
+        sets = []
+        for k in range(nsets):
+            freqs = fr_all[:s_loc].clone()
+            cos, sin = rgg.rope_cossin_precompute(freqs)
+            if h_loc == H:
+                qkv = W.device_normal_bf16((B, s_loc, 3 * H * D), 300 + k, device=dev)
+                xs = [qkv[..., :H * D].view(B, s_loc, H, D),
+                      qkv[..., H * D:2 * H * D].view(B, s_loc, H, D)]
+            else:
+                xs = [W.device_normal_bf16((B, s_loc, h_loc, D), 300 + 2 * k + v, device=dev)
+                      for v in range(2)]
+            outs = [torch.empty((B, s_loc, h_loc, D), dtype=torch.bfloat16, device=dev) for _ in xs]
+            sets.append((freqs, cos, sin, xs, outs))
+        steps = []
+        if h_loc == H:
+            steps.append(("rope_cossin_precompute", pre_b, 1,
+                          [(lambda st=st: rgg.rope_cossin_precompute(st[0], st[1], st[2]))
+                           for st in sets]))
+        steps.append(("rope_rotate_half_bf16", rope_b, 1,
+                      [(lambda st=st: rgg.rope_rotate_half_bf16(st[3], st[1], st[2], out=st[4]))
+                       for st in sets]))
+        for name, nbytes, reads, fns in steps:
+            us, gbps = timed(fns, nbytes)
+            rows_out.append((label, name, nbytes, nsets, us, gbps, stream_us(nbytes, reads)))
+        del sets
+    for split, rows, hid in (("S/8 tokens", g["rows"] // P, g["hidden"]),
+                             ("hidden/8 columns", g["rows"], g["hidden"] // P)):
+        nbytes = rows * hid * 2 * 3
+        nsets = max(2, -(-touch // nbytes))
+        sets = [(W.device_normal_bf16((rows, 2 * hid), 400 + k, g["gate_sigma"], dev),
+                 torch.empty((rows, hid), dtype=torch.bfloat16, device=dev)) for k in range(nsets)]
+        fns = [(lambda st=st: rgg.gelu_and_mul_bf16(st[0], st[1])) for st in sets]
+        us, gbps = timed(fns, nbytes)
+        del sets
+        rows_out.append((f"dit_layer, 1 of {P} ranks ({split})", "gelu_and_mul_bf16", nbytes,
+                         nsets, us, gbps, stream_us(nbytes, 2)))
+    del fr_all
+    torch.cuda.empty_cache()
+
     proj = run_projection()
     print(f"Projection {proj['shape']} (matrix cores, {proj['flops']:.3e} flop per launch)")
     print("| entry point | us per launch | TFLOP/s | % of 2.5 PFLOP/s |")
