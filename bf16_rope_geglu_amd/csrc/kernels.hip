@@ -1142,31 +1142,44 @@ void gemm_gate_up_kernel(GemmParams p)
         asm volatile("" : "+v"(el));
         const int32_t cbase = cn0 + wn * 32;
         const bool live = cbase < p.H;
+        // GEGLU: one wave-wide test picks the table-only path for all 64
+        // gates of a lane (the common case) or the general one; each row
+        // block's 16 table reads then go out together.
+        bool anyg = false;
+        if (Geglu) {
+            bool general = false;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    general |= (bf16_of(acc[i][0][v]) & 0x7FFFu) - 0x0100u >= kLutHi - 0x0100u;
+            anyg = __builtin_amdgcn_ballot_w64(general) != 0;
+        }
 #pragma unroll
         for (int half = 0; half < (Geglu ? 1 : 2); ++half) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                float G[16];
+                if (Geglu) {
+                    if (!anyg) {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            G[v] = __uint_as_float(gelu_common(bf16_of(acc[i][0][v]), lut));
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            G[v] = __uint_as_float(gelu_general(bf16_of(acc[i][0][v]), lut) << 16);
+                    }
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     uint32_t w0, w1;
                     if (Geglu) {
-                        uint32_t g[4], u[4];
-                        float G[4];
-                        bool general = false;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            g[e] = bf16_of(acc[i][0][q * 4 + e]);
-                            u[e] = bf16_of(acc[i][1][q * 4 + e]);
-                            G[e] = __uint_as_float(gelu_common(g[e], lut));
-                            general |= (g[e] & 0x7FFFu) - 0x0100u >= kLutHi - 0x0100u;
-                        }
-                        if (general) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                G[e] = __uint_as_float(gelu_general(g[e], lut) << 16);
-                        }
-                        w0 = rne_pack(bf_lo(u[0]) * G[0], bf_lo(u[1]) * G[1]);
-                        w1 = rne_pack(bf_lo(u[2]) * G[2], bf_lo(u[3]) * G[3]);
+                        const f32x16 &u = acc[i][1];
+                        w0 = rne_pack(bf_lo(bf16_of(u[q * 4 + 0])) * G[q * 4 + 0],
+                                      bf_lo(bf16_of(u[q * 4 + 1])) * G[q * 4 + 1]);
+                        w1 = rne_pack(bf_lo(bf16_of(u[q * 4 + 2])) * G[q * 4 + 2],
+                                      bf_lo(bf16_of(u[q * 4 + 3])) * G[q * 4 + 3]);
                     } else {
                         const f32x16 &a = acc[i][half];
                         w0 = rne_pack(a[q * 4 + 0], a[q * 4 + 1]);
