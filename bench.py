@@ -35,6 +35,11 @@ to each step so the same runs calibrate the counters.
 times only the gate_up projection entry points (and adds the calibration
 copy); --pmc-set projection summarises counters of such runs.
 
+    python bench.py --counter-summary DIR --counter-out FILE
+summarises any other rocprofv3 --pmc passes over `--projection` runs (one
+subfolder per pass): the median per dispatch of each counter for the
+projection kernels and the platform GEMM.
+
     python bench.py --sweep
 prints a markdown table of every kernel on every workload with cold caches
 (replayed from one HIP graph), each beside the streaming reference
@@ -186,9 +191,11 @@ def run_projection(reps=10, warmup=2):
     """The dit_layer projection, x (32768, 4096) times W (2 x 8192, 4096):
     gemm_geglu_bf16 (fused), gemm_bf16_nt alone, gemm_bf16_nt followed by
     gelu_and_mul_bf16 (the unfused path), and torch.matmul (the platform's
-    library GEMM) followed by gelu_and_mul_bf16, for comparison.  Mean of
-    `reps` launches between HIP events on the launch stream; TFLOP/s counts
-    2 M K (2 H) multiply-adds."""
+    library GEMM) followed by gelu_and_mul_bf16, for comparison.  Every case
+    runs `warmup` times first (so the first one timed does not pay for the
+    clock ramp after an idle GPU); then two rounds time each case as the mean
+    of `reps` launches between HIP events on the launch stream, and the
+    faster round is reported.  TFLOP/s counts 2 M K (2 H) multiply-adds."""
     import torch
 
     import bf16_rope_geglu_amd as rgg
@@ -211,19 +218,25 @@ def run_projection(reps=10, warmup=2):
         ("torch.matmul + gelu_and_mul_bf16 (comparison)",
          lambda: (torch.matmul(x, w.t(), out=proj), rgg.gelu_and_mul_bf16(proj, out))),
     ]
+    for _ in range(warmup):
+        for _, fn in cases:
+            fn()
+    torch.cuda.synchronize()
+    best = {}
+    for _ in range(2):
+        for name, fn in cases:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / reps
+            best[name] = min(best.get(name, us), us)
     res = {}
-    for name, fn in cases:
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / reps
+    for name, _ in cases:
+        us = best[name]
         tf = flops / (us * 1e-6) / 1e12
         res[name] = {"us": round(us, 1), "TFLOPs": round(tf, 1),
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
@@ -647,6 +660,46 @@ def pmc_summary(d, out, command="", which="step"):
     print("\n".join(lines))
 
 
+def counter_summary(d, out, command=""):
+    """Median per dispatch (summed over the counter's hardware instances) of
+    every counter found under `d` (one subfolder per rocprofv3 --pmc pass),
+    for the projection kernels and the platform GEMM that `--projection`
+    times beside them."""
+    vals = {}
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                short = _short_kernel(name)
+                if short is None and "Cijk_" in name:
+                    short = "hipBLASLt GEMM (torch.matmul)"
+                if short is None:
+                    continue
+                key = (short, r["Counter_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (k, c, _), v in per.items():
+            vals.setdefault((k, c), []).append(v)
+    kernels = sorted({k for k, _ in vals})
+    counters = sorted({c for _, c in vals})
+    lines = ["# rocprofv3 counters per dispatch (the gate_up projection of the dit_layer workload)",
+             "", f"Commands: `{command}`", "",
+             "| counter | " + " | ".join(kernels) + " |",
+             "|---|" + "---|" * len(kernels)]
+    for c in counters:
+        cells = []
+        for k in kernels:
+            v = sorted(vals.get((k, c), []))
+            cells.append(f"{v[len(v) // 2]:.6g}" if v else "")
+        lines.append(f"| {c} | " + " | ".join(cells) + " |")
+    lines.append("")
+    text = "\n".join(lines)
+    if out:
+        with open(out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 def traffic_for(kernel):
     """Counter bytes of `kernel` from the committed summary, if still current."""
     try:
@@ -677,6 +730,8 @@ def main():
     ap.add_argument("--pmc-set", choices=["step", "projection"], default="step")
     ap.add_argument("--projection", action="store_true",
                     help="time only the gate_up projection entry points (JSON)")
+    ap.add_argument("--counter-summary", metavar="DIR")
+    ap.add_argument("--counter-out", metavar="FILE")
     ap.add_argument("--trace-summary", metavar="DIR")
     ap.add_argument("--trace-out", metavar="FILE")
     ap.add_argument("--command", default="", help="command line recorded in summaries")
@@ -701,6 +756,9 @@ def main():
         return 0
     if args.trace_summary:
         trace_summary(args.trace_summary, args.trace_out, args.command)
+        return 0
+    if args.counter_summary:
+        counter_summary(args.counter_summary, args.counter_out, args.command)
         return 0
     if args.sweep:
         run_sweep()

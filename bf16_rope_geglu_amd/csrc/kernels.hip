@@ -854,58 +854,59 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
 // accumulator, then either stored or turned into up * G(gate) in the
 // epilogue, so the (M, 2H) intermediate never goes to memory.
 //
-// A 512-thread workgroup (two waves per SIMD) computes a 256-row x
-// 128-column block of the output: per 32-wide slice of K it stages 256 rows
-// of x and the 128 gate rows plus the 128 matching up rows of W in LDS.
-// Wave (wm, wn) owns rows wm*128 .. +127 and columns wn*32 .. +31 of both
-// the gate and the up block, so one lane holds the gate and the up
-// accumulator of the same (row, column).  W is the first MFMA operand and x
-// the second, so in a 32x32 block lane l holds output row l % 32 and, in its
-// accumulators v, output columns (v / 4) * 8 + (l / 32) * 4 + v % 4.
-// Operands: lane l supplies row l % 32 of W or of x and the 8 consecutive k
-// at (l / 32) * 8.  The two waves on a SIMD (one of rows 0-127, one of rows
-// 128-255) take turns: while one issues its 16 products on fragments already
-// in registers, the other reads the next slice's fragments and issues its
-// loads, so memory instructions never sit between a wave's products (a wave
-// that issues a global load waits until the CU's address unit takes it).
+// A 256-thread workgroup (one wave per SIMD, its 256 accumulators in the
+// AGPRs) computes a 256-row x 128-column block of the output: per 64-wide
+// slice of K it stages 256 rows of x and the 128 gate rows plus the 128
+// matching up rows of W in LDS.  Wave (wm, wn) owns rows wm*128 .. +127 and
+// columns wn*64 .. +63 of both the gate and the up block, so one lane holds
+// the gate and the up accumulator of the same (row, column).  W is the
+// first MFMA operand and x the second, so in a 32x32 block lane l holds
+// output row l % 32 and, in its accumulators v, output columns
+// (v / 4) * 8 + (l / 32) * 4 + v % 4.  Operands: lane l supplies row l % 32
+// of W or of x and the 8 consecutive k at (l / 32) * 8 of a 16-wide step.
 //
 // Staging uses the direct global-to-LDS load (16 bytes per lane, one 1 KiB
-// run of LDS per instruction: 16 rows of 64 bytes), so the slices never pass
+// run of LDS per instruction: 8 rows of 128 bytes), so the slices never pass
 // through registers.  Rows are unpadded; the 16-byte chunk c of row r sits
-// at chunk c ^ ((r / 4) % 4).  A 16-byte LDS read serves 16 lanes per cycle
+// at chunk c ^ ((r / 2) % 8).  A 16-byte LDS read serves 16 lanes per cycle
 // from 64 four-byte banks; in an operand fetch those lanes read 16
 // consecutive rows at one logical chunk, and the swizzle puts them on 16
-// disjoint 16-byte bank groups (row r starts at group 4 (r % 4)).  Four
-// stages: a wave issues its loads of slice kt + 3 right after reading its
-// fragments of slice kt, so a load has about three slices of products to
-// arrive (the first touch of a line goes to HBM).  A barrier ends every
-// half-turn; before the one after which slice kt + 1 is first read, each
-// wave waits only for its own loads of that slice (loads complete in order),
-// and a stage is reloaded only after both groups have read it.
+// disjoint 16-byte bank groups (row r starts at group 8 (r % 2)).  Two
+// stages of 64 KiB: slice kt + 1 is loaded into one while slice kt is read
+// from the other.
 //
-// The workgroups are persistent (one per CU) and walk the tiles; the block
-// order is remapped so that each XCD (workgroups go to the 8 XCDs round
-// robin) gets one contiguous run of tiles, walked in groups of 8 row blocks
-// with the column block outer, so the tiles an XCD works on at one time
-// share rows of x and of W in its L2.
+// Per slice each wave issues 64 products in 4 steps of 16 (one register
+// set of fragments per step, alternating).  The fragment reads of the next
+// step ride on the first 8 products of each step; the 16 loads of the next
+// slice go out two per three products over the first 24.  After 15
+// products of step 3 the wave waits for its own loads of the next slice
+// (loads complete in order) and passes the barrier that publishes them and
+// frees the stage just read; the last product carries the next slice's
+// step-0 reads.  A late barrier gives the loads the most time to arrive.
+//
+// Workgroups go to the 8 XCDs round robin; the block index is remapped so
+// that each XCD gets one contiguous run of tiles, and the run is walked in
+// groups of 8 row blocks (column block outer), so the tiles an XCD works on
+// at one time share rows of x and of W in its L2.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kGemmThreads = 512;
 constexpr int kGemmBM = 256;              // rows of x per workgroup
 constexpr int kGemmBN = 128;              // gate (and up) columns per workgroup
-constexpr int kGemmBK = 32;               // K slice per stage (64-byte rows)
-constexpr int kGemmStages = 4;
+constexpr int kGemmBK = 64;               // K slice per stage (128-byte rows)
+constexpr int kGemmStages = 2;
 constexpr int kGemmLutBytes = kLutEntries * 2;       // GELU table at LDS offset 0
 constexpr int kGemmOpBytes = 256 * kGemmBK * 2;      // one staged operand (x or W)
 constexpr int kGemmStageBytes = 2 * kGemmOpBytes;
 constexpr size_t kGemmLds = kGemmLutBytes + kGemmStages * kGemmStageBytes;
 constexpr uint32_t kGemmGroupM = 8;
+constexpr int kGemmThreads = 256;
+constexpr int kGemmBarrierAt = 15;        // products of the last step before the barrier
 static_assert(kGemmLds <= 160 * 1024, "LDS of one CU");
 static_assert(kGemmLutBytes % 1024 == 0, "stages start on a 1 KiB boundary");
-static_assert(8 * 128 * 32 * 2 <= 2 * kGemmStageBytes, "epilogue blocks fit stages 2-3");
-static_assert(kLutEntries % 8 == 0 && kLutEntries / 8 <= kGemmThreads, "table: one vector per lane");
+static_assert(4 * 128 * 64 * 2 <= kGemmStageBytes, "epilogue blocks fit stage 1");
+static_assert(kLutEntries % 8 == 0 && kLutEntries / 8 <= 2 * kGemmThreads, "table: two vectors per lane");
 
 __device__ __forceinline__ uint32_t bf16_of(float v) { return rne_pack(v, 0.0f) & 0xFFFFu; }
 
@@ -927,96 +928,107 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, uint32_t t, int64
 }
 
 template <bool Geglu>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_gate_up_kernel(GemmParams p)
 {
-    // [GELU table][stage 0: x | W] .. [stage 3: x | W]
+    // [GELU table][stage 0: x | W][stage 1: x | W]
     extern __shared__ __align__(16) uint8_t gsm[];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wv >> 2, wn = wv & 3;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
     const uint32_t T = p.mblocks * p.nblocks;
 
     // The GELU table goes to LDS now; it is read in the epilogues, after
     // barriers that order these writes before those reads.
-    if (Geglu && tid < (int)(kLutEntries / 8))
-        reinterpret_cast<v4u *>(gsm)[tid] = reinterpret_cast<const v4u *>(g_gelu_lut)[tid];
+    if (Geglu) {
+        constexpr int nv = kLutEntries / 8;
+        const v4u *src = reinterpret_cast<const v4u *>(g_gelu_lut);
+        v4u *dst = reinterpret_cast<v4u *>(gsm);
+        if (tid < nv)
+            dst[tid] = src[tid];
+        if (tid + kGemmThreads < nv)
+            dst[tid + kGemmThreads] = src[tid + kGemmThreads];
+    }
 
-    // Wave w stages row groups 2w, 2w + 1 (16 rows each) of the x tile and of
-    // the W tile (waves 0-3: gate rows, 4-7: up rows): lane i of group g
-    // brings row 16g + i / 4, logical chunk (i % 4) ^ ((i / 16) % 4), to LDS
-    // chunk i % 4 of that row.  The loads address memory as a wave-uniform
-    // base (SGPRs) plus a per-lane 32-bit byte offset fixed for the tile;
-    // offsets stay below 256 row strides; strides are limited to 2^22
-    // elements, which keeps every offset below 2^31.  Rows past M re-read row M-1 and columns past H re-read
-    // column H-1 (not stored).  (The lane index passes through an empty asm
-    // statement so that the compiler recomputes the offsets per tile instead
-    // of keeping loop-invariant copies alive across the tile loop.)
-    uint32_t ox[2], ow[2];
+    // Wave w stages row groups 8w .. 8w + 7 (8 rows each) of the x tile and
+    // of the W tile (waves 0-1: gate rows, 2-3: up rows): lane i of group g
+    // brings row 8g + i / 8, logical chunk (i % 8) ^ ((4g + i / 16) % 8), to
+    // LDS chunk i % 8 of that row.  Rows past M re-read row M-1 and columns
+    // past H re-read column H-1 (not stored).  The loads address memory as a
+    // wave-uniform base (SGPRs: the tile's first x row, the first gate or up
+    // row of this wave's W rows) plus a per-lane 32-bit byte offset fixed for
+    // the tile; the slice only moves the base.  Offsets stay below 256 row
+    // strides; strides are limited to 2^22 elements, which keeps every offset
+    // below 2^31.  (The lane index passes through an empty asm statement so
+    // that the compiler recomputes the offsets per tile instead of keeping
+    // loop-invariant copies alive across the tile loop.)
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t ox[8], ow[8];
     const uint16_t *bx = p.x, *bw = p.w;
     auto point = [&](int64_t m0, int32_t n0) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
         bx = p.x + m0 * p.x_stride;
-        bw = p.w + ((wv < 4 ? 0 : (int64_t)p.H) + n0) * p.w_stride;
+        bw = p.w + ((wv < 2 ? 0 : (int64_t)p.H) + n0) * p.w_stride;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int row = 32 * wv + 16 * j + (ln >> 2);
-            const int chunk = (ln & 3) ^ ((ln >> 4) & 3);
+        for (int j = 0; j < 8; ++j) {
+            const int row = 64 * wv + 8 * j + (ln >> 3);
+            const int chunk = (ln & 7) ^ ((4 * j + (ln >> 4)) & 7);
             const uint32_t m = (uint32_t)(min(m0 + row, p.M - 1) - m0);
             const uint32_t c = (uint32_t)(min(n0 + (row & (kGemmBN - 1)), p.H - 1) - n0);
             ox[j] = m * (uint32_t)p.x_stride * 2u + chunk * 16;
             ow[j] = c * (uint32_t)p.w_stride * 2u + chunk * 16;
         }
     };
-    // One load instruction: row group 2w + (idx & 1) of x (idx < 2) or of W.
+    // One load instruction: row group 8w + idx % 8 of x (idx < 8) or of W.
     // It is written out (M0 holds the LDS address) rather than left to the
     // compiler, which does not know which LDS bytes a direct load writes and
     // would make every later LDS read wait for every load in flight; here
-    // the ordering is explicit: "vmcnt" waits before each barrier, and a
-    // stage is only reloaded after the barrier that ends its last reads.
+    // the ordering is explicit: a "vmcnt" wait before each barrier, and a
+    // stage is only reloaded after the barrier that follows its last reads.
     // The instruction has no register result, and nothing else in this
     // kernel uses M0 (no other LDS-direct, message or relative-move
     // instruction), so setting it here disturbs no compiler state.
-    const uint32_t lds0 = (uint32_t)(uintptr_t)gsm + kGemmLutBytes + wv * 2 * 1024;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)gsm + kGemmLutBytes + wv * 8 * 1024;
     auto dma1 = [&](int kt, int st, int idx) {
-        const int j = idx & 1;
-        const uint16_t *base = (idx < 2 ? bx : bw) + (int64_t)kt * kGemmBK;
-        const uint32_t off = idx < 2 ? ox[j] : ow[j];
-        const uint32_t dst = lds0 + st * kGemmStageBytes + (idx < 2 ? 0 : kGemmOpBytes) + j * 1024;
+        const int j = idx & 7;
+        const uint16_t *base = (idx < 8 ? bx : bw) + (int64_t)kt * kGemmBK;
+        const uint32_t off = idx < 8 ? ox[j] : ow[j];
+        const uint32_t dst = lds0 + st * kGemmStageBytes + (idx < 8 ? 0 : kGemmOpBytes) + j * 1024;
         asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                      :: "v"(off), "s"(base), "s"(dst) : "memory");
     };
     auto fetch = [&](int kt, int st) {
 #pragma unroll
-        for (int idx = 0; idx < 4; ++idx)
+        for (int idx = 0; idx < 16; ++idx)
             dma1(kt, st, idx);
     };
 
-    f32x16 acc[4][2];  // [x row block][gate, up]
+    f32x16 acc[4][4];  // [x row block][gate 0, gate 1, up 0, up 1]
 
-    // Operand fragments of one slice: set 0 for k 0-15, set 1 for k 16-31;
-    // each 4 of x, then the gate and the up fragment of W.
-    const int ra = (wm * 128 + (lane & 31)) * 64;
-    const int rb = (wn * 32 + (lane & 31)) * 64;
-    bf16x8 fa[2][4], fb[2][2];
+    // Operand fragments of one k16 step, double buffered in registers (set
+    // 0 / set 1): 4 of x, then gate 0, gate 1, up 0, up 1 of W.
+    const int ra = (wm * 128 + (lane & 31)) * 128;
+    const int rb = (wn * 64 + (lane & 31)) * 128;
+    bf16x8 fa[2][4], fb[2][4];
     auto frag1 = [&](int st, int ks, int set, int idx) {
         const uint8_t *sx = gsm + kGemmLutBytes + st * kGemmStageBytes;
-        const int ch = ((2 * ks + (lane >> 5)) ^ ((lane >> 2) & 3)) * 16;
+        const int ch = ((2 * ks + (lane >> 5)) ^ (((lane & 31) >> 1) & 7)) * 16;
         if (idx < 4)
-            fa[set][idx] = *reinterpret_cast<const bf16x8 *>(sx + ra + idx * 32 * 64 + ch);
+            fa[set][idx] = *reinterpret_cast<const bf16x8 *>(sx + ra + idx * 32 * 128 + ch);
         else
             fb[set][idx - 4] = *reinterpret_cast<const bf16x8 *>(
-                sx + kGemmOpBytes + rb + (idx - 4) * kGemmBN * 64 + ch);
+                sx + kGemmOpBytes + rb + (((idx - 4) >> 1) * kGemmBN + ((idx - 4) & 1) * 32) * 128 + ch);
     };
+    // Fragments are read in the order the products first use them.
+    constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
     auto mma1 = [&](int set, int idx) {
-        const int i = idx >> 1, j = idx & 1;
+        const int i = idx >> 2, j = idx & 3;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
     };
 
     // The workgroup walks tiles blockIdx.x, + gridDim.x, ... (one workgroup
-    // per CU).  The first two slices of the next tile are requested before
-    // the epilogue of the current one, so their latency hides under it.
+    // per CU).  The first slice of the next tile is requested before the
+    // epilogue of the current one, so its latency hides under it.
     const int KT = p.K / kGemmBK;
     uint32_t tile = blockIdx.x;
     int64_t m0;
@@ -1025,91 +1037,59 @@ void gemm_gate_up_kernel(GemmParams p)
     point(m0, n0);
     if (KT > 0) {
         fetch(0, 0);
-        fetch(min(1, KT - 1), 1);
-        fetch(min(2, KT - 1), 2);
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
     for (;;) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     acc[a][b][v] = 0.0f;
 
-        // Turns: waves 0-3 (group A, rows 0-127) and 4-7 (group B, rows
-        // 128-255) share the SIMDs pairwise and alternate between a compute
-        // half-turn (16 products on fragments already in registers) and a
-        // memory half-turn (the 12 fragment reads of slice s and the 4 loads
-        // of slice s + 3), so a SIMD's matrix pipe always has one wave
-        // feeding it.  A reads slice s + 1 while B multiplies slice s, and
-        // B reads slice s while A multiplies it.  Past the last slice the
-        // loads repeat slice KT - 1 into the stage that already holds it or
-        // into one both groups have finished reading (no branch in the loop).
-        const bool grpA = wv < 4;
-        auto memory = [&](int s_) {
-            if (s_ < KT) {
+        // One slice: product pp = 16 * step + k in the order fixed by
+        // scheduling fences, each followed by at most a fragment read and a
+        // load (the product after the barrier carries the next slice's
+        // reads).  The last slice of a tile loads nothing and passes no
+        // barrier.
+        auto slice = [&](int kt, bool last) {
+            const int st = kt & 1, sn = st ^ 1;
 #pragma unroll
-                for (int idx = 0; idx < 6; ++idx) {
-                    frag1(s_ & 3, 0, 0, idx);
-                    frag1(s_ & 3, 1, 1, idx);
+            for (int pp = 0; pp < 64; ++pp) {
+                const int step = pp >> 4, k = pp & 15;
+                if (step == 3 && k == kGemmBarrierAt && !last) {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    RGG_FENCE();
                 }
+                mma1(step & 1, k);
+                if (step < 3 && k < 8)
+                    frag1(st, step + 1, (step + 1) & 1, kOrder[k]);
+                if (step == 3 && k >= kGemmBarrierAt && !last) {
+                    constexpr int nr = 16 - kGemmBarrierAt;
+                    constexpr int per = (8 + nr - 1) / nr;
+#pragma unroll
+                    for (int r = 0; r < per; ++r) {
+                        const int idx = (k - kGemmBarrierAt) * per + r;
+                        if (idx < 8)
+                            frag1(sn, 0, 0, kOrder[idx]);
+                    }
+                }
+                if (!last && pp < 24 && pp % 3 != 2)
+                    dma1(kt + 1, sn, pp / 3 * 2 + pp % 3);
+                RGG_FENCE();
             }
-            const int kn = min(s_ + 3, KT - 1), sn = (s_ + 3) & 3;
-#pragma unroll
-            for (int idx = 0; idx < 4; ++idx)
-                dma1(kn, sn, idx);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        };
-        auto compute = [&]() {
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                mma1(0, k);
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                mma1(1, k);
-            __builtin_amdgcn_s_setprio(0);
         };
         if (KT > 0) {
-            // before the first turn: A reads slice 0 and loads slice 3
-            if (grpA) {
-                memory(0);
-                asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-            } else {
-                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-            }
-            __builtin_amdgcn_s_barrier();
+#pragma unroll
+            for (int idx = 0; idx < 8; ++idx)
+                frag1(0, 0, 0, kOrder[idx]);
             RGG_FENCE();
-            if (grpA) {
-                for (int s_ = 0; s_ < KT; ++s_) {
-                    compute();                      // A multiplies slice s_
-                    RGG_FENCE();
-                    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-                    __builtin_amdgcn_s_barrier();
-                    RGG_FENCE();
-                    memory(s_ + 1);                 // A reads slice s_ + 1
-                    RGG_FENCE();
-                    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-                    __builtin_amdgcn_s_barrier();
-                    RGG_FENCE();
-                }
-            } else {
-                for (int s_ = 0; s_ < KT; ++s_) {
-                    memory(s_);                     // B reads slice s_
-                    RGG_FENCE();
-                    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-                    __builtin_amdgcn_s_barrier();
-                    RGG_FENCE();
-                    compute();                      // B multiplies slice s_
-                    RGG_FENCE();
-                    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-                    __builtin_amdgcn_s_barrier();
-                    RGG_FENCE();
-                }
-            }
+            for (int kt = 0; kt + 1 < KT; ++kt)
+                slice(kt, false);
+            slice(KT - 1, true);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();  // every wave is done with the operand stages
@@ -1121,73 +1101,73 @@ void gemm_gate_up_kernel(GemmParams p)
         if (more) {
             gemm_tile(p, next, m0, n0);
             point(m0, n0);
-            if (KT > 0) {
+            if (KT > 0)
                 fetch(0, 0);
-                fetch(min(1, KT - 1), 1);
-            }
         }
 
         // Epilogue: round each accumulator to bf16 (the projection's
         // output), then keep it, or form rne(up * G(gate)).  Each wave writes
-        // its 128 x 32 block of results to its 8 KiB of stages 2-3 as 64-byte
-        // rows (16-byte chunk c of row r at chunk c ^ ((r / 4) % 4); four
+        // its 128 x 64 block of results to its 16 KiB of stage 1 as
+        // 128-byte rows (16-byte chunk c of row r at chunk c ^ (r % 8); four
         // adjacent columns per 8-byte write), then reads it back as 16-byte
-        // vectors, four lanes per row, for 64-byte global stores.  The plain
-        // product does this twice: gate columns, then up columns (H further
-        // along the row).  H is a multiple of 64, so a wave's 32 columns are
-        // wholly inside [0, H) or outside.
+        // vectors, eight lanes per row, for whole-line global stores.  The
+        // plain product does this twice: gate columns, then up columns (H
+        // further along the row).  H is a multiple of 64, so a wave's block
+        // is wholly inside [0, H) or outside.
         const uint16_t *lut = reinterpret_cast<const uint16_t *>(gsm);
-        uint8_t *ep = gsm + kGemmLutBytes + 2 * kGemmStageBytes + wv * 8192;
+        uint8_t *ep = gsm + kGemmLutBytes + kGemmStageBytes + wave * 16384;
         int el = lane;
         asm volatile("" : "+v"(el));
-        const int32_t cbase = cn0 + wn * 32;
+        const int32_t cbase = cn0 + wn * 64;
         const bool live = cbase < p.H;
-        // GEGLU: one wave-wide test picks the table-only path for all 64
-        // gates of a lane (the common case) or the general one; each row
-        // block's 16 table reads then go out together.
         bool anyg = false;
         if (Geglu) {
             bool general = false;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    general |= (bf16_of(acc[i][0][v]) & 0x7FFFu) - 0x0100u >= kLutHi - 0x0100u;
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        general |= (bf16_of(acc[i][cb][v]) & 0x7FFFu) - 0x0100u >= kLutHi - 0x0100u;
             anyg = __builtin_amdgcn_ballot_w64(general) != 0;
         }
 #pragma unroll
         for (int half = 0; half < (Geglu ? 1 : 2); ++half) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float G[16];
-                if (Geglu) {
-                    if (!anyg) {
 #pragma unroll
-                        for (int v = 0; v < 16; ++v)
-                            G[v] = __uint_as_float(gelu_common(bf16_of(acc[i][0][v]), lut));
-                    } else {
-#pragma unroll
-                        for (int v = 0; v < 16; ++v)
-                            G[v] = __uint_as_float(gelu_general(bf16_of(acc[i][0][v]), lut) << 16);
-                    }
-                }
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t w0, w1;
+                for (int cb = 0; cb < 2; ++cb) {
+                    float G[16];
                     if (Geglu) {
-                        const f32x16 &u = acc[i][1];
-                        w0 = rne_pack(bf_lo(bf16_of(u[q * 4 + 0])) * G[q * 4 + 0],
-                                      bf_lo(bf16_of(u[q * 4 + 1])) * G[q * 4 + 1]);
-                        w1 = rne_pack(bf_lo(bf16_of(u[q * 4 + 2])) * G[q * 4 + 2],
-                                      bf_lo(bf16_of(u[q * 4 + 3])) * G[q * 4 + 3]);
-                    } else {
-                        const f32x16 &a = acc[i][half];
-                        w0 = rne_pack(a[q * 4 + 0], a[q * 4 + 1]);
-                        w1 = rne_pack(a[q * 4 + 2], a[q * 4 + 3]);
+                        if (!anyg) {
+#pragma unroll
+                            for (int v = 0; v < 16; ++v)
+                                G[v] = __uint_as_float(gelu_common(bf16_of(acc[i][cb][v]), lut));
+                        } else {
+#pragma unroll
+                            for (int v = 0; v < 16; ++v)
+                                G[v] = __uint_as_float(gelu_general(bf16_of(acc[i][cb][v]), lut) << 16);
+                        }
                     }
-                    const int r = i * 32 + (el & 31);
-                    *reinterpret_cast<uint2 *>(ep + r * 64 + ((q ^ ((r >> 2) & 3)) << 4) +
-                                               (el >> 5) * 8) = make_uint2(w0, w1);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uint32_t w0, w1;
+                        if (Geglu) {
+                            const f32x16 &u = acc[i][2 + cb];
+                            w0 = rne_pack(bf_lo(bf16_of(u[q * 4 + 0])) * G[q * 4 + 0],
+                                          bf_lo(bf16_of(u[q * 4 + 1])) * G[q * 4 + 1]);
+                            w1 = rne_pack(bf_lo(bf16_of(u[q * 4 + 2])) * G[q * 4 + 2],
+                                          bf_lo(bf16_of(u[q * 4 + 3])) * G[q * 4 + 3]);
+                        } else {
+                            const f32x16 &a = acc[i][2 * half + cb];
+                            w0 = rne_pack(a[q * 4 + 0], a[q * 4 + 1]);
+                            w1 = rne_pack(a[q * 4 + 2], a[q * 4 + 3]);
+                        }
+                        const int r = i * 32 + (el & 31), chunk = cb * 4 + q;
+                        *reinterpret_cast<uint2 *>(ep + r * 128 + ((chunk ^ (r & 7)) << 4) +
+                                                   (el >> 5) * 8) = make_uint2(w0, w1);
+                    }
                 }
             }
             // A wave reads back only its own block, and LDS operations of
@@ -1196,9 +1176,9 @@ void gemm_gate_up_kernel(GemmParams p)
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             uint16_t *ob = p.out + (half ? p.H : 0) + cbase;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int rr = (el >> 2) + 16 * k, cv = el & 3;
-                const v4u val = *reinterpret_cast<const v4u *>(ep + rr * 64 + ((cv ^ ((rr >> 2) & 3)) << 4));
+            for (int k = 0; k < 16; ++k) {
+                const int rr = (el >> 3) + 8 * k, cv = el & 7;
+                const v4u val = *reinterpret_cast<const v4u *>(ep + rr * 128 + ((cv ^ (rr & 7)) << 4));
                 const int64_t row = cm0 + wm * 128 + rr;
                 if (live && row < p.M)
                     *reinterpret_cast<v4u *>(ob + row * p.out_stride + cv * 8) = val;
@@ -1208,13 +1188,12 @@ void gemm_gate_up_kernel(GemmParams p)
         if (!more)
             break;
         tile = next;
-        // Every wave has left its block area (stages 2-3): slice 2 of the new
-        // tile may go to stage 2 once slices 0 and 1 (and this tile's stores)
-        // are in; the second barrier makes slices 0 and 1 visible to all.
+        // The first barrier: every wave has left its block area in stage 1,
+        // which the new tile's slice 1 will fill.  Then each wave waits for
+        // its loads of slice 0 (and this tile's stores), and the second
+        // barrier makes slice 0 visible to all.
         __builtin_amdgcn_s_barrier();
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (KT > 0)
-            fetch(min(2, KT - 1), 2);
         __builtin_amdgcn_s_barrier();
     }
 }
@@ -1337,7 +1316,7 @@ hipError_t launch_gelu_and_mul(const GegluParams &p, int grid, hipStream_t strea
 
 hipError_t launch_gemm_gate_up(const GemmParams &p, bool geglu, hipStream_t stream)
 {
-    // The four stages and the table take 135 KiB of LDS, above the 64 KiB a
+    // The two stages and the table take 135 KiB of LDS, above the 64 KiB a
     // launch gets without asking.  The attribute is set once per device (it
     // belongs to the kernel as loaded on the current device).
     constexpr int kMaxDevices = 64;
