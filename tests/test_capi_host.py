@@ -412,3 +412,32 @@ def test_projection_bytes_and_trace_names():
     assert bench._short_kernel(
         "void rgg::(anonymous namespace)::rope_rotate_half_kernel<true, false>(rgg::RopeParams)") \
         == "rope_rotate_half_kernel"
+
+
+def test_counter_summary_medians(tmp_path):
+    """bench.py --counter-summary: per dispatch, a counter's hardware
+    instances are summed; across dispatches the median is kept; passes in
+    separate folders merge; the platform GEMM gets its own column."""
+    sys.path.insert(0, ROOT)
+    import bench
+    head = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+    plain = "void rgg::(anonymous namespace)::gemm_gate_up_kernel<false>(rgg::GemmParams)"
+    blas = "Custom_Cijk_Alik_Bljk_BBS_MT256x256x64_gfx950"
+    rows1 = [(1, plain, "GRBM_GUI_ACTIVE", 10), (1, plain, "GRBM_GUI_ACTIVE", 5),
+             (2, plain, "GRBM_GUI_ACTIVE", 30), (3, plain, "GRBM_GUI_ACTIVE", 20),
+             (4, blas, "GRBM_GUI_ACTIVE", 7), (5, "other_kernel", "GRBM_GUI_ACTIVE", 99)]
+    rows2 = [(1, plain, "MfmaUtil", 60.0), (2, plain, "MfmaUtil", 70.0), (3, plain, "MfmaUtil", 80.0)]
+    for name, rows in (("p1", rows1), ("p2", rows2)):
+        d = tmp_path / name
+        d.mkdir()
+        (d / "x_counter_collection.csv").write_text(
+            head + "".join(f'{a},"{b}",{c},{v}\n' for a, b, c, v in rows))
+    out = tmp_path / "summary.md"
+    bench.counter_summary(str(tmp_path), str(out), "cmd")
+    text = out.read_text()
+    table = {ln.split("|")[1].strip(): [c.strip() for c in ln.strip().strip("|").split("|")[1:]]
+             for ln in text.splitlines() if ln.startswith("| ") and not ln.startswith("| counter")}
+    header = [c.strip() for c in text.splitlines()[4].strip().strip("|").split("|")[1:]]
+    assert header == ["gemm_gate_up_kernel<false>", "hipBLASLt GEMM (torch.matmul)"]
+    assert table["GRBM_GUI_ACTIVE"] == ["20", "7"]      # dispatch 1 sums to 15; median of 15, 30, 20
+    assert table["MfmaUtil"] == ["70", ""]
