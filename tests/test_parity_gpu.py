@@ -868,6 +868,28 @@ def test_gemm_full_size(orc):
                            "full size projection, gaussian")
 
 
+@pytest.mark.parametrize("K", [64, 192, 320])
+def test_gemm_several_tiles_per_workgroup(orc, K):
+    """More output tiles than workgroups (17 x 16 = 272, ragged last row
+    block), so workgroups walk several tiles in turn, with K of 1, 3 and 5
+    slices of 64 (an odd count ends a tile in the other LDS stage):
+    exact-sum inputs bit-exact with the oracle, fused and plain, on rows
+    sampled from every row block."""
+    M, H = 17 * 256 - 3, 16 * 128
+    rng = np.random.Generator(np.random.PCG64(9700 + K))
+    rsel = np.unique(np.concatenate([np.arange(0, M, 256), np.arange(255, M, 256),
+                                     rng.integers(0, M, 8), [M - 1]]))
+    rs = torch.from_numpy(rsel).cuda()
+    say(f"gemm several tiles per workgroup: {M} x {K} x {2 * H}, {len(rsel)} rows")
+    x = W.device_small_int_bf16((M, K), 9700 + K)
+    w = W.device_small_int_bf16((2 * H, K), 9800 + K)
+    fused = rgg.gemm_geglu_bf16(x, w)
+    plain = rgg.gemm_bf16_nt(x, w)
+    hx, hw = host(x[rs]), host(w)
+    assert_bitexact(host(fused[rs]), orc.gemm_geglu(hx, hw), f"several tiles fused K={K}")
+    assert_bitexact(host(plain[rs]), orc.gemm_bf16(hx, hw), f"several tiles projection K={K}")
+
+
 # ---------------------------------------------------------------------------
 # layouts, limits, graphs
 # ---------------------------------------------------------------------------
