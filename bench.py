@@ -22,7 +22,8 @@ GEMM followed by gelu_and_mul_bf16 for comparison (TFLOP/s against the
 
 `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload (16384 tokens, 8192 GEGLU rows): `value` on one thread, and
-`all_cores` with the sample split over every core the process may use.  `roofline.traffic` comes from the committed rocprofv3
+`all_cores` with the sample split over every core the process may use;
+`cpu` names the host CPU model.  `roofline.traffic` comes from the committed rocprofv3
 counter summary for the dominant kernel, and is null if the kernel source has
 changed since the counters were taken.
 
@@ -520,7 +521,20 @@ def run_cpu_baseline(wid, tokens=16384, geglu_rows=8192):
                    f"{dt:.2f} s on one thread"),
         "all_cores": {"value": round(nbytes / dt_n / 1e9, 4), "unit": "GB/s", "cores": n,
                       "seconds": round(dt_n, 2)},
+        "cpu": _cpu_model(),
     }
+
+
+def _cpu_model():
+    """The host CPU's model name, as /proc/cpuinfo gives it (None if absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 # ---------------------------------------------------------------------------
