@@ -265,7 +265,8 @@ def stream_ref_library():
     lib = ctypes.CDLL(path)
     lib.rgg_stream_ref.restype = ctypes.c_int
     lib.rgg_stream_ref.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                   ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
@@ -320,7 +321,7 @@ def run_sweep(reps=40, touch=2 << 30):
             a = st[0].data_ptr() if reads >= 1 else None
             b = st[1].data_ptr() if reads == 2 else None
             status = ref.rgg_stream_ref(a, b, st[-1].data_ptr(), wbytes // 16,
-                                        block, torch.cuda.current_stream(dev).cuda_stream)
+                                        block, 1, 0, 3, torch.cuda.current_stream(dev).cuda_stream)
             if status:
                 raise RuntimeError(f"rgg_stream_ref returned {status}")
         best = min(timed([(lambda st=st, blk=blk: launch(st, blk)) for st in sets], nbytes)[0]
