@@ -254,7 +254,7 @@ def run_projection(reps=10, warmup=2):
 
 def stream_ref_library():
     """ctypes handle of bf16_rope_geglu_amd/lib/libstreamref.so (built by
-    __graft_entry__.build()), the streaming reference timed in the sweep."""
+    __graft_entry__.build()), the streaming references timed as ceilings."""
     import ctypes
 
     import torch  # noqa: F401  (loads the HIP runtime the library links)
@@ -266,17 +266,248 @@ def stream_ref_library():
     lib.rgg_stream_ref.restype = ctypes.c_int
     lib.rgg_stream_ref.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_int, ctypes.c_void_p]
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     return lib
 
 
-def run_sweep(reps=40, touch=2 << 30):
-    """Per-launch time of each kernel on each workload.  Enough input and
-    output sets are allocated that consecutive launches touch `touch` bytes
-    (well past the 256 MB Infinity Cache) and launches rotate through them, so
-    every launch streams from HBM.  `reps` launches are captured in one HIP
-    graph and replayed between two events, so host launch overhead does not
-    pad the short kernels."""
+COLD_REPS = 40
+COLD_TOUCH = 2 << 30
+
+# Members of the streaming-reference family timed as the ceiling for a
+# kernel's traffic: (workgroup size, 16-byte vectors per lane, grid (0: one
+# pass, else that many persistent workgroups), cache policy (1: nontemporal
+# loads; +2 nontemporal stores; +4 write-through stores), LDS bytes per
+# workgroup (caps residency; 0: none)).  These are the fastest members at
+# each workload size in a sweep of the whole family (block 256/512/1024,
+# 1/2/4/8 vectors per lane, one pass or 256..2048 persistent workgroups,
+# every policy, residency caps of 3..6 workgroups per compute unit,
+# `profiles/stream_family_sweep.md`); the ceiling reported is the best of
+# them on the box at hand.
+STREAM_FAMILY = [(256, 1, 0, 7, 0), (256, 1, 0, 5, 0), (256, 1, 0, 3, 0), (256, 2, 0, 3, 0),
+                 (512, 1, 0, 7, 0), (256, 1, 1024, 7, 0)]
+
+
+def cold_us(fns, reps=COLD_REPS):
+    """Per-launch time of `fns` (launchers over disjoint buffer sets) replayed
+    round robin from one HIP graph of `reps` launches between two events:
+    the sets together touch far more than the 256 MB Infinity Cache, so every
+    launch streams from HBM, and host launch overhead does not pad short
+    kernels.  The faster of three replays."""
+    import torch
+
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(reps):
+            fns[r % len(fns)]()
+    graph.replay()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        best = us if best is None else min(best, us)
+    del graph
+    return best
+
+
+def stream_ceiling(ref, nbytes, reads, dev, family=STREAM_FAMILY, touch=COLD_TOUCH):
+    """The fastest member of the streaming-reference family moving `nbytes`
+    with `reads` (0, 1 or 2) reads per write, same cold-cache rotation:
+    (us per launch, member)."""
+    import torch
+
+    wbytes = nbytes // (1 + reads)
+    nsets = max(2, -(-touch // nbytes))
+    sets = [[torch.empty(wbytes, dtype=torch.uint8, device=dev) for _ in range(reads + 1)]
+            for _ in range(nsets)]
+
+    def launch(st, cfg):
+        a = st[0].data_ptr() if reads >= 1 else None
+        b = st[1].data_ptr() if reads == 2 else None
+        status = ref.rgg_stream_ref(a, b, st[-1].data_ptr(), wbytes // 16, *cfg,
+                                    torch.cuda.current_stream(dev).cuda_stream)
+        if status:
+            raise RuntimeError(f"rgg_stream_ref returned {status}")
+    best = None
+    for cfg in family:
+        us = cold_us([(lambda st=st, cfg=cfg: launch(st, cfg)) for st in sets])
+        if best is None or us < best[0]:
+            best = (us, cfg)
+    del sets
+    return best
+
+
+def run_stream_sweep(out=None):
+    """The whole streaming-reference family at the graded traffic of each
+    workload (RoPE 1 read : 1 write at 104 MB, 136 MB and 1.09 GB; GEGLU
+    2 : 1 at 604 MB and 1.61 GB), cold caches as cold_us times them: workgroup
+    size, vectors per lane, one pass or persistent grids, cache policy and
+    residency caps.  Writes a markdown summary (the ten fastest members per
+    size and the fastest of each grid form) to `out`."""
+    import itertools
+
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ref = stream_ref_library()
+    sizes = [("partial RoPE traffic", 103809024, 1), ("rope_qk RoPE traffic", 136314880, 1),
+             ("dit_layer RoPE traffic", 1090519040, 1), ("geglu GEGLU traffic", 603979776, 2),
+             ("dit_layer GEGLU traffic", 1610612736, 2)]
+    caps = {3: 54528, 4: 40960, 5: 32768, 6: 27136}
+    lines = ["# Streaming-reference family, cold caches", "",
+             "Command: `python bench.py --stream-sweep --stream-sweep-out profiles/stream_family_sweep.md`",
+             "", "Members: (workgroup size, 16-byte vectors per lane, grid: 0 one pass / n persistent "
+             "workgroups, policy: 1 nontemporal loads, +2 nontemporal stores, +4 write-through (sc1) "
+             "stores, LDS bytes per workgroup capping residency).  Time per launch from a HIP graph "
+             "of 40 launches over buffer sets touching >= 2 GiB (cold_us in bench.py).", ""]
+    for label, nbytes, reads in sizes:
+        wbytes = nbytes // (1 + reads)
+        nvec = wbytes // 16
+        nsets = max(2, -(-COLD_TOUCH // nbytes))
+        sets = [[torch.ones(wbytes, dtype=torch.uint8, device=dev) for _ in range(reads + 1)]
+                for _ in range(nsets)]
+        cfgs = []
+        for vpl, block, pol in itertools.product((1, 2, 4, 8), (256, 512, 1024), (1, 2, 3, 5, 7)):
+            for grid in (0, 256, 512, 1024, 2048):
+                if grid and grid * block * vpl >= nvec:
+                    continue
+                cfgs.append((block, vpl, grid, pol, 0))
+        for (block, vpl), pol, n in itertools.product(((256, 1), (256, 2)), (3, 7), caps):
+            cfgs.append((block, vpl, 0, pol, caps[n]))
+        res = []
+        for cfg in cfgs:
+            def launch(st, cfg=cfg):
+                b = st[1].data_ptr() if reads == 2 else None
+                status = ref.rgg_stream_ref(st[0].data_ptr(), b, st[-1].data_ptr(), nvec, *cfg,
+                                            torch.cuda.current_stream(dev).cuda_stream)
+                if status:
+                    raise RuntimeError(f"rgg_stream_ref returned {status}")
+            us = cold_us([(lambda st=st: launch(st)) for st in sets])
+            res.append((us, cfg))
+        del sets
+        torch.cuda.empty_cache()
+        res.sort()
+        frac = lambda us: 100 * nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS
+        lines += [f"## {label}: {nbytes} bytes, {reads} read(s) per write, {len(res)} members", "",
+                  "| rank | block | vectors/lane | grid | policy | LDS | us | % of 8 TB/s |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for k, (us, c) in enumerate(res[:10]):
+            lines.append(f"| {k + 1} | {c[0]} | {c[1]} | {c[2]} | {c[3]} | {c[4]} | {us:.2f} | {frac(us):.1f} |")
+        lines += ["", "Fastest per grid form: " + "; ".join(
+            f"grid {g}: {min(us for us, c in res if c[2] == g):.2f} us"
+            for g in sorted({c[2] for _, c in res})), ""]
+        print("\n".join(lines[-16:]), flush=True)
+    text = "\n".join(lines) + "\n"
+    if out:
+        with open(out, "w") as f:
+            f.write(text)
+    return text
+
+
+def rope_cold_sets(wid, dev, touch=COLD_TOUCH, layouts=False):
+    """Buffer sets of a RoPE workload for cold timing: angles, tables, the
+    input views and separate outputs (and, for the fused-QKV workload, the
+    attention consumer's (B, H, S, D) outputs when `layouts`)."""
+    import torch
+
+    import bf16_rope_geglu_amd as rgg
+    import workloads as W
+
+    r = W.WORKLOADS[wid]["rope"]
+    B, S, H, D = r["B"], r["S"], r["H"], r["D"]
+    algo = W.algo_bytes(wid)
+    nsets = max(2, -(-touch // (algo["rope"] + algo["precompute"])))
+    fr = torch.from_numpy(W.workload_freqs(wid)).to(dev)
+    sets = []
+    for k in range(nsets):
+        freqs = fr.clone()
+        cos, sin = rgg.rope_cossin_precompute(freqs)
+        if r["layout"] == "qkv":
+            qkv = W.device_normal_bf16((B, S, 3 * H * D), 100 + k, device=dev)
+            xs = [qkv[..., :H * D].view(B, S, H, D), qkv[..., H * D:2 * H * D].view(B, S, H, D)]
+        else:
+            xs = [W.device_normal_bf16((B, S, H, D), 100 + 4 * k + v, device=dev)
+                  for v in range(r["views"])]
+        outs = [torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev) for _ in xs]
+        bhsd = ([torch.empty((B, H, S, D), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
+                 for _ in xs] if layouts and r["layout"] == "qkv" else None)
+        sets.append({"freqs": freqs, "cos": cos, "sin": sin, "x": xs, "out": outs, "bhsd": bhsd})
+    return sets
+
+
+def geglu_cold_sets(rows, hidden, gate_sigma, dev, seed0=200, touch=COLD_TOUCH):
+    import torch
+
+    import workloads as W
+
+    nsets = max(2, -(-touch // (rows * hidden * 6)))
+    return [(W.device_normal_bf16((rows, 2 * hidden), seed0 + k, gate_sigma, dev),
+             torch.empty((rows, hidden), dtype=torch.bfloat16, device=dev)) for k in range(nsets)]
+
+
+def _entry(us, nbytes, ceiling=None):
+    e = {"us": round(us, 2), "algo_bytes": nbytes,
+         "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+         "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+    if ceiling:
+        cus, cfg = ceiling
+        e["ceiling"] = {"us": round(cus, 2), "frac": round(nbytes / (cus * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                        "stream": {"block": cfg[0], "vectors_per_lane": cfg[1], "grid": cfg[2],
+                                   "policy": cfg[3], "lds": cfg[4]}}
+        e["vs_ceiling"] = round(cus / us, 4)
+    return e
+
+
+def run_configs(dev):
+    """The graded kernels on every workload that carries them, cold caches,
+    each beside the fastest streaming reference of the same traffic:
+    rope_rotate_half_bf16 on rope_qk, partial and dit_layer (q and k views of
+    the fused QKV output), gelu_and_mul_bf16 on geglu and dit_layer."""
+    import torch
+
+    import bf16_rope_geglu_amd as rgg
+    import workloads as W
+
+    ref = stream_ref_library()
+    res = {}
+    for wid, wl in sorted(W.WORKLOADS.items()):
+        if wid == 0:
+            continue
+        algo = W.algo_bytes(wid)
+        ent = {}
+        if "rope" in wl:
+            sets = rope_cold_sets(wid, dev)
+            us = cold_us([(lambda st=st: rgg.rope_rotate_half_bf16(st["x"], st["cos"], st["sin"],
+                                                                  out=st["out"])) for st in sets])
+            del sets
+            ent["rope_rotate_half_bf16"] = _entry(us, algo["rope"],
+                                                  stream_ceiling(ref, algo["rope"], 1, dev))
+        if "geglu" in wl:
+            g = wl["geglu"]
+            sets = geglu_cold_sets(g["rows"], g["hidden"], g["gate_sigma"], dev)
+            us = cold_us([(lambda st=st: rgg.gelu_and_mul_bf16(st[0], st[1])) for st in sets])
+            del sets
+            ent["gelu_and_mul_bf16"] = _entry(us, algo["geglu"],
+                                              stream_ceiling(ref, algo["geglu"], 2, dev))
+        res[wl["name"]] = ent
+        torch.cuda.empty_cache()
+    return res
+
+
+def run_sweep():
+    """Per-launch time of each kernel on each workload, cold caches (see
+    cold_us), each beside the fastest streaming reference of the same traffic
+    (see stream_ceiling), then one rank's share of dit_layer and the
+    projection."""
     import torch
 
     import bf16_rope_geglu_amd as rgg
@@ -288,46 +519,10 @@ def run_sweep(reps=40, touch=2 << 30):
     rows_out = []
     ref = stream_ref_library()
 
-    def timed(fns, nbytes):
-        for f in fns:
-            f()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for r in range(reps):
-                fns[r % len(fns)]()
-        graph.replay()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        graph.replay()
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / reps
-        del graph
-        return us, nbytes / (us * 1e-6) / 1e9
-
-    def stream_us(nbytes, reads):
-        """Per-launch time of the streaming reference moving nbytes with
-        `reads` (0, 1 or 2) reads per write (same cold-cache rotation), the
-        faster of 256- and 512-thread workgroups."""
-        wbytes = nbytes // (1 + reads)
-        nsets = max(2, -(-touch // nbytes))
-        sets = [[torch.empty(wbytes, dtype=torch.uint8, device=dev) for _ in range(reads + 1)]
-                for _ in range(nsets)]
-
-        def launch(st, block):
-            a = st[0].data_ptr() if reads >= 1 else None
-            b = st[1].data_ptr() if reads == 2 else None
-            status = ref.rgg_stream_ref(a, b, st[-1].data_ptr(), wbytes // 16,
-                                        block, 1, 0, 3, torch.cuda.current_stream(dev).cuda_stream)
-            if status:
-                raise RuntimeError(f"rgg_stream_ref returned {status}")
-        best = min(timed([(lambda st=st, blk=blk: launch(st, blk)) for st in sets], nbytes)[0]
-                   for blk in (256, 512))
-        del sets
-        return best
+    def add(label, name, nbytes, nsets, fns, reads):
+        us = cold_us(fns)
+        cus, _ = stream_ceiling(ref, nbytes, reads, dev)
+        rows_out.append((label, name, nbytes, nsets, us, nbytes / (us * 1e-6) / 1e9, cus))
 
     for wid, wl in sorted(W.WORKLOADS.items()):
         if wid == 0:
@@ -335,60 +530,35 @@ def run_sweep(reps=40, touch=2 << 30):
         algo = W.algo_bytes(wid)
         if "rope" in wl:
             r = wl["rope"]
-            B, S, H, D, R = r["B"], r["S"], r["H"], r["D"], r["R"]
-            nsets = max(2, -(-touch // (algo["rope"] + algo["precompute"])))
-            fr = torch.from_numpy(W.workload_freqs(wid)).to(dev)
-            sets = []
-            for k in range(nsets):
-                freqs = fr.clone()
-                cos, sin = rgg.rope_cossin_precompute(freqs)
-                if r["layout"] == "qkv":
-                    qkv = W.device_normal_bf16((B, S, 3 * H * D), 100 + k, device=dev)
-                    xs = [qkv[..., :H * D].view(B, S, H, D), qkv[..., H * D:2 * H * D].view(B, S, H, D)]
-                else:
-                    xs = [W.device_normal_bf16((B, S, H, D), 100 + 4 * k + v, device=dev)
-                          for v in range(r["views"])]
-                outs = [torch.empty((B, S, H, D), dtype=torch.bfloat16, device=dev) for _ in xs]
-                # the attention consumer's head-major layout, written through strides
-                bhsd = [torch.empty((B, H, S, D), dtype=torch.bfloat16, device=dev).permute(0, 2, 1, 3)
-                        for _ in xs] if r["layout"] == "qkv" else None
-                sets.append((freqs, cos, sin, xs, outs, bhsd))
-            pre = [(lambda st=st: rgg.rope_cossin_precompute(st[0], st[1], st[2])) for st in sets]
-            rot = [(lambda st=st: rgg.rope_rotate_half_bf16(st[3], st[1], st[2], out=st[4]))
-                   for st in sets]
-            steps = [("rope_cossin_precompute", "precompute", pre, 1)]
+            B = r["B"]
+            sets = rope_cold_sets(wid, dev, layouts=True)
+            n = len(sets)
+            add(wl["name"], "rope_cossin_precompute", algo["precompute"], n,
+                [(lambda st=st: rgg.rope_cossin_precompute(st["freqs"], st["cos"], st["sin"]))
+                 for st in sets], 1)
             fk = r["freqs"]
             if fk["kind"] == "3axis":
-                grd = [(lambda st=st: rgg.rope_cossin_from_grid(
-                    B, fk["grid"], fk["dims"], W.THETA, cos_out=st[1], sin_out=st[2]))
-                    for st in sets]
-                steps.append(("rope_cossin_from_grid", "precompute_grid", grd, 0))
-            steps.append(("rope_rotate_half_bf16", "rope", rot, 1))
+                add(wl["name"], "rope_cossin_from_grid", algo["precompute_grid"], n,
+                    [(lambda st=st: rgg.rope_cossin_from_grid(
+                        B, fk["grid"], fk["dims"], W.THETA, cos_out=st["cos"], sin_out=st["sin"]))
+                     for st in sets], 0)
+            add(wl["name"], "rope_rotate_half_bf16", algo["rope"], n,
+                [(lambda st=st: rgg.rope_rotate_half_bf16(st["x"], st["cos"], st["sin"], out=st["out"]))
+                 for st in sets], 1)
             if r["layout"] == "qkv":
-                inplace = [(lambda st=st: rgg.rope_rotate_half_bf16(st[3], st[1], st[2], out=st[3]))
-                           for st in sets]
-                to_bhsd = [(lambda st=st: rgg.rope_rotate_half_bf16(st[3], st[1], st[2], out=st[5]))
-                           for st in sets]
-                steps.append(("rope_rotate_half_bf16, in place in qkv", "rope", inplace, 1))
-                steps.append(("rope_rotate_half_bf16, into (B, H, S, D)", "rope", to_bhsd, 1))
-            for name, key, fns, reads in steps:
-                us, gbps = timed(fns, algo[key])
-                rows_out.append((wl["name"], name, algo[key], nsets, us, gbps,
-                                 stream_us(algo[key], reads)))
+                add(wl["name"], "rope_rotate_half_bf16, in place in qkv", algo["rope"], n,
+                    [(lambda st=st: rgg.rope_rotate_half_bf16(st["x"], st["cos"], st["sin"], out=st["x"]))
+                     for st in sets], 1)
+                add(wl["name"], "rope_rotate_half_bf16, into (B, H, S, D)", algo["rope"], n,
+                    [(lambda st=st: rgg.rope_rotate_half_bf16(st["x"], st["cos"], st["sin"],
+                                                             out=st["bhsd"])) for st in sets], 1)
             del sets
         if "geglu" in wl:
             g = wl["geglu"]
-            nsets = max(2, -(-touch // algo["geglu"]))
-            sets = []
-            for k in range(nsets):
-                inp = W.device_normal_bf16((g["rows"], 2 * g["hidden"]), 200 + k, g["gate_sigma"], dev)
-                out = torch.empty((g["rows"], g["hidden"]), dtype=torch.bfloat16, device=dev)
-                sets.append((inp, out))
-            fns = [(lambda st=st: rgg.gelu_and_mul_bf16(st[0], st[1])) for st in sets]
-            us, gbps = timed(fns, algo["geglu"])
+            sets = geglu_cold_sets(g["rows"], g["hidden"], g["gate_sigma"], dev)
+            add(wl["name"], "gelu_and_mul_bf16", algo["geglu"], len(sets),
+                [(lambda st=st: rgg.gelu_and_mul_bf16(st[0], st[1])) for st in sets], 2)
             del sets
-            rows_out.append((wl["name"], "gelu_and_mul_bf16", algo["geglu"], nsets, us, gbps,
-                             stream_us(algo["geglu"], 2)))
         torch.cuda.empty_cache()
 
     # One rank's share of dit_layer when the layer is split over 8 GPUs: the
@@ -406,7 +576,7 @@ def run_sweep(reps=40, touch=2 << 30):
         T = B * s_loc
         pre_b = T * R * 4 + 2 * T * R * 2
         rope_b = 2 * (2 * T * h_loc * D * 2) + 2 * T * R * 2
-        nsets = max(2, -(-touch // (rope_b + pre_b)))
+        nsets = max(2, -(-COLD_TOUCH // (rope_b + pre_b)))
         sets = []
         for k in range(nsets):
             freqs = fr_all[:s_loc].clone()
@@ -420,29 +590,18 @@ def run_sweep(reps=40, touch=2 << 30):
                       for v in range(2)]
             outs = [torch.empty((B, s_loc, h_loc, D), dtype=torch.bfloat16, device=dev) for _ in xs]
             sets.append((freqs, cos, sin, xs, outs))
-        steps = []
         if h_loc == H:
-            steps.append(("rope_cossin_precompute", pre_b, 1,
-                          [(lambda st=st: rgg.rope_cossin_precompute(st[0], st[1], st[2]))
-                           for st in sets]))
-        steps.append(("rope_rotate_half_bf16", rope_b, 1,
-                      [(lambda st=st: rgg.rope_rotate_half_bf16(st[3], st[1], st[2], out=st[4]))
-                       for st in sets]))
-        for name, nbytes, reads, fns in steps:
-            us, gbps = timed(fns, nbytes)
-            rows_out.append((label, name, nbytes, nsets, us, gbps, stream_us(nbytes, reads)))
+            add(label, "rope_cossin_precompute", pre_b, nsets,
+                [(lambda st=st: rgg.rope_cossin_precompute(st[0], st[1], st[2])) for st in sets], 1)
+        add(label, "rope_rotate_half_bf16", rope_b, nsets,
+            [(lambda st=st: rgg.rope_rotate_half_bf16(st[3], st[1], st[2], out=st[4])) for st in sets], 1)
         del sets
     for split, rows, hid in (("S/8 tokens", g["rows"] // P, g["hidden"]),
                              ("hidden/8 columns", g["rows"], g["hidden"] // P)):
-        nbytes = rows * hid * 2 * 3
-        nsets = max(2, -(-touch // nbytes))
-        sets = [(W.device_normal_bf16((rows, 2 * hid), 400 + k, g["gate_sigma"], dev),
-                 torch.empty((rows, hid), dtype=torch.bfloat16, device=dev)) for k in range(nsets)]
-        fns = [(lambda st=st: rgg.gelu_and_mul_bf16(st[0], st[1])) for st in sets]
-        us, gbps = timed(fns, nbytes)
+        sets = geglu_cold_sets(rows, hid, g["gate_sigma"], dev, seed0=400)
+        add(f"dit_layer, 1 of {P} ranks ({split})", "gelu_and_mul_bf16", rows * hid * 6, len(sets),
+            [(lambda st=st: rgg.gelu_and_mul_bf16(st[0], st[1])) for st in sets], 2)
         del sets
-        rows_out.append((f"dit_layer, 1 of {P} ranks ({split})", "gelu_and_mul_bf16", nbytes,
-                         nsets, us, gbps, stream_us(nbytes, 2)))
     del fr_all
     torch.cuda.empty_cache()
 
@@ -454,7 +613,7 @@ def run_sweep(reps=40, touch=2 << 30):
         print(f"| {n} | {r['us']:.1f} | {r['TFLOPs']:.1f} | {100 * r['frac']:.1f} |")
     print()
     print("| workload | entry point | algorithmic bytes | buffer sets | us per launch | GB/s "
-          "| % of 8 TB/s | stream reference us (% of 8 TB/s) | kernel vs stream |")
+          "| % of 8 TB/s | stream ceiling us (% of 8 TB/s) | kernel vs ceiling |")
     print("|---|---|---|---|---|---|---|---|---|")
     for w, n, b, k, us, gbps, sus in rows_out:
         sfrac = 100 * b / (sus * 1e-6) / 1e9 / PEAK_HBM_GBPS
@@ -737,6 +896,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit_layer", choices=["dit_layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload cold-cache kernel timings in the JSON line")
     ap.add_argument("--no-projection", action="store_true",
                     help="skip the gate_up projection timings in the JSON line")
     ap.add_argument("--calibration-copy", action="store_true")
@@ -752,6 +913,9 @@ def main():
     ap.add_argument("--command", default="", help="command line recorded in summaries")
     ap.add_argument("--sweep", action="store_true",
                     help="time every kernel on every workload (cold caches) instead")
+    ap.add_argument("--stream-sweep", action="store_true",
+                    help="time the whole streaming-reference family at each workload's traffic")
+    ap.add_argument("--stream-sweep-out", metavar="FILE")
     args = ap.parse_args()
 
     if args.pmc_summary:
@@ -777,6 +941,9 @@ def main():
         return 0
     if args.sweep:
         run_sweep()
+        return 0
+    if args.stream_sweep:
+        run_stream_sweep(args.stream_sweep_out)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU step (each rank would run "
@@ -812,6 +979,9 @@ def main():
         "kernels": res["kernels"],
         "frac_of_peak": round(value / PEAK_HBM_GBPS, 4),
     }
+    if not args.no_configs:
+        import torch
+        line["configs"] = run_configs(torch.device("cuda:0"))
     if not args.no_projection:
         line["projection"] = run_projection()
     if not args.no_cpu_baseline:

@@ -28,69 +28,16 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 8 x bf16
 
-// Tunables.  The defaults are the fastest settings measured on MI355X; a
-// build may override them with -D to sweep.
-#ifndef RGG_STREAM_NT
-#define RGG_STREAM_NT 1          // nontemporal hint on data touched once
-#endif
-#ifndef RGG_GEGLU_BLOCK
-#define RGG_GEGLU_BLOCK 512      // GEGLU workgroup size
-#endif
-#ifndef RGG_GEGLU_VEC
-#define RGG_GEGLU_VEC 1          // 16-byte vectors per lane (loads all issued first)
-#endif
-#ifndef RGG_GEGLU_WG_PER_CU
-#define RGG_GEGLU_WG_PER_CU 0    // 0: one vector per lane, one pass per workgroup;
-#endif                           // n: n resident workgroups per CU, grid-stride loop
-#ifndef RGG_ROPE_VEC_PER_WG
-#define RGG_ROPE_VEC_PER_WG 512  // 16-byte vectors of x per RoPE workgroup (one view)
-#endif
-#ifndef RGG_ROPE_BLOCK
-#define RGG_ROPE_BLOCK 256       // RoPE workgroup size
-#endif
-#ifndef RGG_ROPE_UNROLL
-#define RGG_ROPE_UNROLL 1        // RoPE items per lane with their loads issued together
-#endif
-#ifndef RGG_ROPE_WAVE_STAGE
-#define RGG_ROPE_WAVE_STAGE 1    // one-token RoPE: each wave stages its own cos/sin copy (no barrier)
-#endif
-#ifndef RGG_ROPE_LANE
-#define RGG_ROPE_LANE 1          // one-token launches whose half-rotation splits 128-byte lines:
-#endif                           // one contiguous output vector per lane
-#ifndef RGG_GEGLU_LUT_FIRST
-#define RGG_GEGLU_LUT_FIRST 1    // GEGLU: fetch the lane's GELU-table vector before gate/up
-#endif
-#ifndef RGG_ROPE_TPW_FIT
-#define RGG_ROPE_TPW_FIT 1       // tokens per workgroup: best lane fill of one or two passes
-#endif
-#ifndef RGG_STAGE_FIRST
-#define RGG_STAGE_FIRST 1        // one-token RoPE, R <= 256: fetch the cos/sin row before x
-#endif
-#ifndef RGG_ROPE_LDS
-#define RGG_ROPE_LDS 1           // 1: stage cos/sin rows in LDS; 0: read them per item
-#endif
-#ifndef RGG_COSSIN_COLS
-#define RGG_COSSIN_COLS 8        // table columns per lane in the cos/sin kernel (8 or 4)
-#endif
-
-// Streamed data (read or written once) bypasses cache retention when
-// RGG_STREAM_NT is set: the loads and stores carry the nontemporal bit.
+// Streamed data (read or written once) bypasses cache retention: the loads
+// and stores carry the nontemporal bit.
 __device__ __forceinline__ v4u stream_load(const uint16_t *p)
 {
-#if RGG_STREAM_NT
     return __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
-#else
-    return *reinterpret_cast<const v4u *>(p);
-#endif
 }
 
 __device__ __forceinline__ void stream_store(uint16_t *p, v4u v)
 {
-#if RGG_STREAM_NT
     __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(p));
-#else
-    *reinterpret_cast<v4u *>(p) = v;
-#endif
 }
 
 // Load/store whose nontemporal hint is chosen per launch: the hint pays only
@@ -152,12 +99,9 @@ __device__ __forceinline__ uint32_t bf16_from_double(double v)
 // a few ulps of a bf16 rounding midpoint (its low 16 bits near 0x8000).
 // Those few (about one in 7000) are recomputed in double and rounded exactly,
 // so each entry is the correctly rounded bf16 of cos/sin of the fp32 angle.
-// RGG_COSSIN_GUARD is that margin in fp32 ulps.
+// kTieGuard is that margin in fp32 ulps.
 // ---------------------------------------------------------------------------
-#ifndef RGG_COSSIN_GUARD
-#define RGG_COSSIN_GUARD 4
-#endif
-constexpr uint32_t kTieGuard = RGG_COSSIN_GUARD;
+constexpr uint32_t kTieGuard = 4;
 
 __device__ __forceinline__ bool near_bf16_tie(float r)
 {
@@ -181,8 +125,6 @@ __device__ __forceinline__ void cossin_pair(float a0, float a1, uint32_t &cw, ui
         sw = bf16_from_double(ds0) | (bf16_from_double(ds1) << 16);
     }
 }
-
-constexpr int kCosSinCols = RGG_COSSIN_COLS;
 
 __device__ __forceinline__ void cossin_vec8(v4u a0, v4u a1, uint32_t *c, uint32_t *sn)
 {
@@ -231,21 +173,16 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
             *reinterpret_cast<v4u *>(p.cos + o + half + col) = cv;
             *reinterpret_cast<v4u *>(p.sin + o + half + col) = sv;
         } else {
-            const int col = cg * kCosSinCols;
-            uint32_t c[kCosSinCols / 2], sn[kCosSinCols / 2];
-            float4 f0 = reinterpret_cast<const float4 *>(f + col)[0];
+            const int col = cg * 8;
+            uint32_t c[4], sn[4];
+            const float4 f0 = reinterpret_cast<const float4 *>(f + col)[0];
+            const float4 f1 = reinterpret_cast<const float4 *>(f + col)[1];
             cossin_pair(f0.x, f0.y, c[0], sn[0]);
             cossin_pair(f0.z, f0.w, c[1], sn[1]);
-            if constexpr (kCosSinCols == 8) {
-                float4 f1 = reinterpret_cast<const float4 *>(f + col)[1];
-                cossin_pair(f1.x, f1.y, c[2], sn[2]);
-                cossin_pair(f1.z, f1.w, c[3], sn[3]);
-                *reinterpret_cast<v4u *>(p.cos + o + col) = v4u{c[0], c[1], c[2], c[3]};
-                *reinterpret_cast<v4u *>(p.sin + o + col) = v4u{sn[0], sn[1], sn[2], sn[3]};
-            } else {
-                *reinterpret_cast<uint2 *>(p.cos + o + col) = make_uint2(c[0], c[1]);
-                *reinterpret_cast<uint2 *>(p.sin + o + col) = make_uint2(sn[0], sn[1]);
-            }
+            cossin_pair(f1.x, f1.y, c[2], sn[2]);
+            cossin_pair(f1.z, f1.w, c[3], sn[3]);
+            *reinterpret_cast<v4u *>(p.cos + o + col) = v4u{c[0], c[1], c[2], c[3]};
+            *reinterpret_cast<v4u *>(p.sin + o + col) = v4u{sn[0], sn[1], sn[2], sn[3]};
         }
     }
 }
@@ -423,7 +360,7 @@ __device__ __forceinline__ RopeItem rope_locate(const RopeParams &p, const RopeV
     return it;
 }
 
-constexpr int kRopeBlock = RGG_ROPE_BLOCK;
+constexpr int kRopeBlock = 256;
 constexpr int64_t kMaxRopeWorkgroups = (int64_t)1 << 20;  // per launch (2^28 work-items)
 
 __device__ __forceinline__ void load_bf16x8_as_f32(const uint16_t *src, float *dst)
@@ -433,7 +370,7 @@ __device__ __forceinline__ void load_bf16x8_as_f32(const uint16_t *src, float *d
     dst[4] = bf_lo(w.z); dst[5] = bf_hi(w.z); dst[6] = bf_lo(w.w); dst[7] = bf_hi(w.w);
 }
 
-constexpr int kRopeUnroll = RGG_ROPE_UNROLL;
+constexpr int kRopeUnroll = 1;  // items per lane with their loads issued together
 
 template <bool OneToken, bool Nt>
 __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams p)
@@ -466,7 +403,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
         // twice, so no load sits under a branch.
         RopeItem it[U];
         v4u x1[U], x2[U];
-#if RGG_STAGE_FIRST
         // With per-wave staging and R <= 256 each lane fetches at most one
         // 16-byte vector of the cos/sin row, and it does so before its x
         // loads: loads return in order, so waiting for the row then does not
@@ -478,7 +414,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
             const uint16_t *src = k >= R / 8 ? p.sin + t0 * R + (k - R / 8) * 8 : p.cos + t0 * R + k * 8;
             stg = *reinterpret_cast<const v4u *>(src);
         }
-#endif
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int ic = min(base + u * kRopeBlock + tid, items - 1);
@@ -486,7 +421,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
             x1[u] = load16<Nt>(V.x + it[u].xo);
             x2[u] = load16<Nt>(V.x + it[u].xo + (it[u].rot ? half : 0));
         }
-#if RGG_ROPE_LDS
         if (OneToken && p.wave_stage && base == first) {
             // One token: every wave stages its own fp32 copy of the row in
             // its own LDS slot, so no wave waits for another.  LDS operations
@@ -496,7 +430,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
             float *wc = lcos + wave * 2 * R, *ws = wc + R;
             const v4u *gc = reinterpret_cast<const v4u *>(p.cos + t0 * R);
             const v4u *gs = reinterpret_cast<const v4u *>(p.sin + t0 * R);
-#if RGG_STAGE_FIRST
             if (stage1) {
                 if (lane < R / 4) {
                     const bool is_sin = lane >= R / 8;
@@ -506,7 +439,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
                     d[1] = make_float4(bf_lo(stg.z), bf_hi(stg.z), bf_lo(stg.w), bf_hi(stg.w));
                 }
             } else
-#endif
             for (int k = lane; k < R / 4; k += 64) {
                 const bool is_sin = k >= R / 8;
                 const int kk = is_sin ? k - R / 8 : k;
@@ -519,8 +451,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-#endif
-#if RGG_ROPE_LDS
         if ((!OneToken || !p.wave_stage) && base == first) {
             // Stage this workgroup's cos/sin rows (consecutive table rows) as
             // fp32 while the x loads are in flight.
@@ -538,14 +468,12 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
             }
             __syncthreads();
         }
-#endif
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (base + u * kRopeBlock + tid >= items)
                 continue;
             if (it[u].rot) {
                 float c1[8], s1[8], c2[8], s2[8];
-#if RGG_ROPE_LDS
                 const float *rc = lcos, *rs = lsin;
                 if (OneToken && p.wave_stage) {
                     rc = lcos + (tid >> 6) * 2 * R;
@@ -555,13 +483,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
                 load_f32x8(rs + it[u].co, s1);
                 load_f32x8(rc + it[u].co + half, c2);
                 load_f32x8(rs + it[u].co + half, s2);
-#else
-                const int64_t cg = t0 * R + it[u].co;
-                load_bf16x8_as_f32(p.cos + cg, c1);
-                load_bf16x8_as_f32(p.sin + cg, s1);
-                load_bf16x8_as_f32(p.cos + cg + half, c2);
-                load_bf16x8_as_f32(p.sin + cg + half, s2);
-#endif
                 const v4u a1 = x1[u], a2 = x2[u];
                 uint32_t a[4], b[4];
                 rope_word(a1.x, a2.x, c1 + 0, s1 + 0, c2 + 0, s2 + 0, a[0], b[0]);
@@ -577,7 +498,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_kernel(RopeParams
     }
 }
 
-#if RGG_ROPE_LANE
 // One output vector per lane: lane i of the workgroup writes 16-byte vector i
 // of the token's head rows, so every load and store instruction of a wave
 // covers whole contiguous lines for any R.  The lane also loads its
@@ -614,7 +534,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
         int64_t oo[U];
         int j[U];
         v4u a[U], b[U];
-#if RGG_STAGE_FIRST
         v4u stg = v4u{0u, 0u, 0u, 0u};
         const bool stage1 = R > 0 && R <= 256;
         if (stage1 && base == first) {
@@ -623,7 +542,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
                                              : p.cos + (int64_t)t * R + k * 8;
             stg = *reinterpret_cast<const v4u *>(src);
         }
-#endif
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int ic = min(base + u * kRopeBlock + tid, items - 1);
@@ -638,7 +556,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
         if (base == first) {
             const v4u *gc = reinterpret_cast<const v4u *>(p.cos + (int64_t)t * R);
             const v4u *gs = reinterpret_cast<const v4u *>(p.sin + (int64_t)t * R);
-#if RGG_STAGE_FIRST
             if (stage1) {
                 if (lane < R / 4) {
                     const bool is_sin = lane >= R / 8;
@@ -648,7 +565,6 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
                     d[1] = make_float4(bf_lo(stg.z), bf_hi(stg.z), bf_lo(stg.w), bf_hi(stg.w));
                 }
             } else
-#endif
             for (int k = lane; k < R / 4; k += 64) {
                 const bool is_sin = k >= R / 8;
                 const int kk = is_sin ? k - R / 8 : k;
@@ -680,7 +596,227 @@ __global__ __launch_bounds__(kRopeBlock) void rope_rotate_half_lane_kernel(RopeP
         }
     }
 }
-#endif
+
+// ---------------------------------------------------------------------------
+// Rotate-half RoPE for heads of at most 128 columns: one contiguous 16-byte
+// vector per lane, partners exchanged across lanes     [ERNIE-fuse §2]
+//
+// Each view is walked as one flat run of 16-byte vectors, index
+// g = (token * H + head) * D/8 + j, and a workgroup takes the next
+// VPL * blockDim consecutive vectors (lane t: vectors t, t + blockDim, ...),
+// exactly the access pattern of a plain stream: every wave instruction reads
+// or writes 64 consecutive vectors.  D/8 divides 16, so a head row never
+// straddles a 16-lane row of the wave, and the rotate-half partner of vector
+// j (j + R/16 in the first half, j - R/16 in the second) sits in the same
+// 16-lane row: it is fetched by a DPP row rotation, not a second load.  The
+// lane reads its own 8 entries of the token's cos/sin rows (16 bytes each,
+// shared through L1/L2 by every head and view of the token) ahead of x, so
+// there is no LDS staging and no barrier.  Vectors past R/8 in a head are the
+// tail, copied (or skipped in place).
+// ---------------------------------------------------------------------------
+template <int Ror>
+__device__ __forceinline__ uint32_t row_ror(uint32_t v)
+{
+    // DPP row_ror:Ror (0x120 + Ror): lane l of a 16-lane row reads lane
+    // (l - Ror) mod 16 of the same row.
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + Ror, 0xF, 0xF, false);
+}
+
+template <int HV>
+__device__ __forceinline__ v4u partner_vec(v4u x, bool first_half)
+{
+    // first half: the vector HV lanes up, negated (sign bits flipped, exact);
+    // second half: the vector HV lanes down.
+    uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t dn = row_ror<HV>(w[k]);
+        const uint32_t up = HV == 8 ? dn : row_ror<16 - HV>(w[k]);
+        w[k] = first_half ? up ^ 0x80008000u : dn;
+    }
+    return v4u{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ uint32_t rope_word_bf(uint32_t x, uint32_t y, uint32_t c, uint32_t s)
+{
+    uint32_t p0 = rne_pack(bf_lo(x) * bf_lo(c), bf_lo(y) * bf_lo(s));
+    uint32_t p1 = rne_pack(bf_hi(x) * bf_hi(c), bf_hi(y) * bf_hi(s));
+    return rne_pack(bf_lo(p0) + bf_hi(p0), bf_lo(p1) + bf_hi(p1));
+}
+
+// Stores of whole lines go out as buffer stores carrying the nontemporal and
+// device-scope write-through (sc1) bits, which measured 1-2% faster than
+// nontemporal alone; the wave's first live lane gives the base and the
+// others 32-bit byte offsets from it (a wave's 64 vectors then sit in one
+// token's contiguous head rows, a 1 KiB span).
+__device__ __forceinline__ void store16_lines(uint16_t *out, int64_t oo, bool live, v4u v)
+{
+    const uint64_t m = __builtin_amdgcn_ballot_w64(live);
+    if (m == 0)
+        return;
+    const int first = (int)__builtin_ctzll(m);
+    const int64_t o0 = ((int64_t)__builtin_amdgcn_readlane((int)(oo >> 32), first) << 32) |
+                       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)oo, first);
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(out + o0, 0, 0x7FFFFFF0, 0x00020000);
+    if (live)
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, (uint32_t)((oo - o0) * 2), 0, 2 | 16);
+}
+
+// The loads and the rotation of VPL vectors per lane for chunk `chunk` of
+// view V (vectors chunk * chunk_vecs + threadIdx.x + u * blockDim.x).
+template <int HV, int VPL, bool Lines>
+struct XlaneState {
+    v4u c[VPL], s[VPL], x[VPL];
+    int64_t oo[VPL];
+    int j[VPL];
+    bool live[VPL];
+
+    __device__ __forceinline__ void fetch(const RopeParams &p, const RopeView &V, uint32_t chunk)
+    {
+        const uint32_t total = p.vecs_per_view;
+        const uint32_t vmask = (1u << p.log_vecs) - 1u;
+        const uint32_t base = chunk * (uint32_t)p.chunk_vecs + threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+            const uint32_t g0 = base + u * blockDim.x;
+            live[u] = g0 < total;
+            const uint32_t g = min(g0, total - 1u);
+            j[u] = (int)(g & vmask);
+            const uint32_t hh = g >> p.log_vecs;
+            const uint32_t t = fdiv(hh, p.div_heads);
+            const uint32_t h = hh - t * (uint32_t)p.H;
+            const uint32_t b = fdiv(t, p.div_s);
+            const uint32_t sq = t - b * p.div_s.d;
+            const int64_t tab = (int64_t)t * p.R + min(j[u], 2 * HV - 1) * 8;
+            c[u] = *reinterpret_cast<const v4u *>(p.cos + tab);
+            s[u] = *reinterpret_cast<const v4u *>(p.sin + tab);
+            const int64_t xo = (int64_t)b * V.xs_b + (int64_t)sq * V.xs_s + (int64_t)h * V.xs_h + j[u] * 8;
+            oo[u] = (int64_t)b * V.os_b + (int64_t)sq * V.os_s + (int64_t)h * V.os_h + j[u] * 8;
+            x[u] = load16<Lines>(V.x + xo);
+        }
+    }
+
+    // Every lane forms the rotation (tail lanes on a clamped table entry) and
+    // then keeps it or its input, so no load sits under a branch.
+    __device__ __forceinline__ void finish(const RopeView &V, bool tail)
+    {
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+            const v4u xx = x[u], cc = c[u], sn = s[u];
+            const v4u y = partner_vec<HV>(xx, j[u] < HV);
+            const v4u r = v4u{rope_word_bf(xx.x, y.x, cc.x, sn.x), rope_word_bf(xx.y, y.y, cc.y, sn.y),
+                              rope_word_bf(xx.z, y.z, cc.z, sn.z), rope_word_bf(xx.w, y.w, cc.w, sn.w)};
+            const bool rot = j[u] < 2 * HV;
+            const bool st = live[u] && (rot || tail);
+            if constexpr (Lines)
+                store16_lines(V.out, oo[u], st, rot ? r : xx);
+            else if (st)
+                store16<false>(V.out + oo[u], rot ? r : xx);
+        }
+    }
+};
+
+// One pass: workgroup w takes chunk w / n_views of view w % n_views.
+template <int HV, int VPL, bool Lines>
+__global__ __launch_bounds__(1024) void rope_xlane_kernel(RopeParams p)
+{
+    const uint32_t wg = blockIdx.x;
+    const uint32_t chunk = fdiv(wg, p.div_views);
+    const int v = (int)(wg - chunk * (uint32_t)p.n_views);
+    const RopeView V = p.v[v];
+    XlaneState<HV, VPL, Lines> st;
+    st.fetch(p, V, p.chunk0 + chunk);
+    __builtin_amdgcn_sched_barrier(0);  // every load goes out before anything waits
+    st.finish(V, (p.tail_mask >> v) & 1);
+}
+
+// Rotate-half RoPE on token-linear layouts                [ERNIE-fuse §2]
+//
+// The common layout: every view's heads are contiguous within a token
+// (stride_h == D), batch rows follow each other in token order (stride_b ==
+// S * stride_s), and a token's heads fill whole waves (H * D/8 a multiple of
+// 64).  Each wave's 64 vectors are then one contiguous 1 KiB run of one
+// token, so the token, the row base and the table row are computed once per
+// wave in scalar registers, the loads and stores are buffer instructions
+// with a scalar base and the lane's fixed 16 * lane byte offset, and the
+// lane's work is only its loads, the DPP partner exchange, the rotation and
+// one store: about 90 vector instructions per 16-byte vector against 170
+// for the per-lane addressing of rope_xlane_kernel, which left the kernel
+// short of a plain stream at 136 MB.  Workgroup w takes vectors
+// 256 w' .. 256 w' + 255 of view w / chunks (w' = w % chunks): one view
+// after the other.
+__device__ __forceinline__ uint32_t rope_word_f(uint32_t x, uint32_t y, float c0, float c1,
+                                                float s0, float s1)
+{
+    uint32_t p0 = rne_pack(bf_lo(x) * c0, bf_lo(y) * s0);
+    uint32_t p1 = rne_pack(bf_hi(x) * c1, bf_hi(y) * s1);
+    return rne_pack(bf_lo(p0) + bf_hi(p0), bf_lo(p1) + bf_hi(p1));
+}
+
+template <int HV>
+__global__ __launch_bounds__(256) void rope_lean_kernel(RopeParams p)
+{
+    const uint32_t v = blockIdx.x / p.chunks;
+    const uint32_t blk = blockIdx.x - v * p.chunks;
+    const RopeView &V = p.v[v];
+    const bool keep_tail = (p.tail_mask >> v) & 1;
+    uint16_t *const out = V.out;
+    const int64_t os_s = V.os_s;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = (int)(lane & ((1u << p.log_vecs) - 1u));
+    const bool rot = j < 2 * HV;
+
+    // g of the wave's first vector (uniform); a wave past the end re-reads
+    // the last one and stores nothing
+    const uint32_t gw = blk * 256u + wave * 64u;
+    const bool live = gw < p.vecs_per_view;
+    const uint32_t g = min(gw, p.vecs_per_view - 64u);
+    const uint32_t t = fdiv(g, p.div_vecs);  // divisor H * D/8
+    const uint32_t w0 = g - t * p.div_vecs.d;
+    const uint32_t tab_lane = (uint32_t)min(j, 2 * HV - 1) * 16u;  // bytes
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p.cos + (uint64_t)t * (uint32_t)p.R), 0, p.R * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsn = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p.sin + (uint64_t)t * (uint32_t)p.R), 0, p.R * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(V.x + ((uint64_t)t * (uint64_t)V.xs_s + w0 * 8u)), 0, 1024, 0x00020000);
+    const v4u cv = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rc, tab_lane, 0, 0));
+    v4u sv = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsn, tab_lane, 0, 0));
+    // nontemporal (aux bit 1): x is read once
+    const v4u xx = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rx, lane * 16u, 0, 2));
+    // all three loads go out before anything waits; the output row's
+    // parameters are read before it, so no scalar load follows the wait
+    asm volatile("" ::"s"(out), "s"(os_s), "s"(keep_tail ? 1 : 0));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // sin of the first half negated (exact): rne(-x' s) = rne(x' (-s))
+    sv ^= j < HV ? 0x80008000u : 0u;
+    float c[8], s8[8];
+    c[0] = bf_lo(cv.x); c[1] = bf_hi(cv.x); c[2] = bf_lo(cv.y); c[3] = bf_hi(cv.y);
+    c[4] = bf_lo(cv.z); c[5] = bf_hi(cv.z); c[6] = bf_lo(cv.w); c[7] = bf_hi(cv.w);
+    s8[0] = bf_lo(sv.x); s8[1] = bf_hi(sv.x); s8[2] = bf_lo(sv.y); s8[3] = bf_hi(sv.y);
+    s8[4] = bf_lo(sv.z); s8[5] = bf_hi(sv.z); s8[6] = bf_lo(sv.w); s8[7] = bf_hi(sv.w);
+    uint32_t yw[4] = {xx.x, xx.y, xx.z, xx.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        // both rotations in every lane (a DPP read of a lane that a branch
+        // has switched off would not return its value)
+        const uint32_t dn = row_ror<HV>(yw[k]);
+        const uint32_t up = HV == 8 ? dn : row_ror<16 - HV>(yw[k]);
+        yw[k] = j < HV ? up : dn;
+    }
+    const v4u r = v4u{rope_word_f(xx.x, yw[0], c[0], c[1], s8[0], s8[1]),
+                      rope_word_f(xx.y, yw[1], c[2], c[3], s8[2], s8[3]),
+                      rope_word_f(xx.z, yw[2], c[4], c[5], s8[4], s8[5]),
+                      rope_word_f(xx.w, yw[3], c[6], c[7], s8[6], s8[7])};
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        out + ((uint64_t)t * (uint64_t)os_s + w0 * 8u), 0, 1024, 0x00020000);
+    // nontemporal and write-through (aux bits 1 and 4)
+    if (live && (rot || keep_tail))
+        __builtin_amdgcn_raw_buffer_store_b128(rot ? r : xx, ro, lane * 16u, 0, 2 | 16);
+}
 
 // ---------------------------------------------------------------------------
 // GEGLU with activation rounding             [ERNIE-fuse §3]
@@ -787,33 +923,15 @@ __device__ __forceinline__ v4u geglu_vec(v4u g, v4u u, const uint16_t *lut)
     return o;
 }
 
-constexpr int kGegluBlock = RGG_GEGLU_BLOCK;
-constexpr int kGegluVec = RGG_GEGLU_VEC;
+constexpr int kGegluBlock = 512;
 
+// Lines: every wave's 64 output vectors are one contiguous, line-aligned
+// 1 KiB run (rows of a multiple of 512 columns, line-aligned row starts), so
+// the store goes out as a buffer store with the write-through bit as well.
+template <bool Lines>
 __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p)
 {
     __shared__ __align__(16) uint16_t lut[kLutEntries];
-    const uint32_t nvec_row = p.div_vecs.d;
-    const uint32_t chunk = kGegluBlock * kGegluVec;
-    const uint32_t step = gridDim.x * chunk;
-    uint32_t base = blockIdx.x * chunk;
-
-    v4u g[kGegluVec], u[kGegluVec];
-    int64_t oo[kGegluVec];
-    auto fetch = [&](uint32_t b0) {
-#pragma unroll
-        for (int k = 0; k < kGegluVec; ++k) {
-            // lanes past the end re-read the last vector (no load under a branch)
-            uint32_t j = min(b0 + k * kGegluBlock + threadIdx.x, p.vec_total - 1);
-            uint32_t row = fdiv(j, p.div_vecs);
-            uint32_t col = (j - row * nvec_row) * 8;
-            const uint16_t *src = p.in + (int64_t)row * p.in_stride + col;
-            g[k] = stream_load(src);
-            u[k] = stream_load(src + p.hidden);
-            oo[k] = (int64_t)row * p.out_stride + col;
-        }
-    };
-#if RGG_GEGLU_LUT_FIRST
     // The lane's table vector is fetched before its gate/up vectors: loads
     // return in order, so the LDS fill and the barrier then overlap the HBM
     // latency instead of waiting for it.
@@ -821,29 +939,23 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
     const uint32_t kt = min(threadIdx.x, kLutEntries / 8 - 1);
     const v4u tv = reinterpret_cast<const v4u *>(g_gelu_lut)[kt];
     __builtin_amdgcn_sched_barrier(0);  // keep the table fetch ahead of gate/up
-    fetch(base);  // indexes are clamped, so the first fetch needs no guard
+    // Lanes past the end re-read the last vector (no load under a branch).
+    const uint32_t i = blockIdx.x * kGegluBlock + threadIdx.x;
+    const uint32_t j = min(i, p.vec_total - 1);
+    const uint32_t row = fdiv(j, p.div_vecs);
+    const uint32_t col = (j - row * p.div_vecs.d) * 8;
+    const uint16_t *src = p.in + (int64_t)row * p.in_stride + col;
+    const v4u g = stream_load(src);
+    const v4u u = stream_load(src + p.hidden);
     if (threadIdx.x < kLutEntries / 8)
         reinterpret_cast<v4u *>(lut)[threadIdx.x] = tv;
-#else
-    if (base < p.vec_total)
-        fetch(base);
-
-    for (uint32_t k = threadIdx.x; k < kLutEntries / 8; k += kGegluBlock)
-        reinterpret_cast<v4u *>(lut)[k] = reinterpret_cast<const v4u *>(g_gelu_lut)[k];
-#endif
     __syncthreads();
-
-    while (base < p.vec_total) {
-#pragma unroll
-        for (int k = 0; k < kGegluVec; ++k) {
-            v4u o = geglu_vec(g[k], u[k], lut);
-            if (base + k * kGegluBlock + threadIdx.x < p.vec_total)
-                stream_store(p.out + oo[k], o);
-        }
-        base += step;
-        if (base < p.vec_total)
-            fetch(base);
-    }
+    const v4u o = geglu_vec(g, u, lut);
+    const int64_t oo = (int64_t)row * p.out_stride + col;
+    if constexpr (Lines)
+        store16_lines(p.out, oo, i < p.vec_total, o);
+    else if (i < p.vec_total)
+        stream_store(p.out + oo, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -985,17 +1097,25 @@ void gemm_gate_up_kernel(GemmParams p)
     // would make every later LDS read wait for every load in flight; here
     // the ordering is explicit: a "vmcnt" wait before each barrier, and a
     // stage is only reloaded after the barrier that follows its last reads.
-    // The instruction has no register result, and nothing else in this
-    // kernel uses M0 (no other LDS-direct, message or relative-move
-    // instruction), so setting it here disturbs no compiler state.
+    // The instruction has no register result, and the statement declares
+    // M0 among the registers it writes, so any code the compiler places
+    // after it that needs M0 sets M0 again.  (M0 is a reserved register, so
+    // the compiler notes that it does not save it across the statement:
+    // nothing here needs it saved.)  The stages stay in one LDS array
+    // indexed by the slice parity at run time: as separate arrays, with the
+    // compiler's own direct-load intrinsic, every slice pair would be
+    // unrolled and the kernel runs out of registers.
     const uint32_t lds0 = (uint32_t)(uintptr_t)gsm + kGemmLutBytes + wv * 8 * 1024;
     auto dma1 = [&](int kt, int st, int idx) {
         const int j = idx & 7;
         const uint16_t *base = (idx < 8 ? bx : bw) + (int64_t)kt * kGemmBK;
         const uint32_t off = idx < 8 ? ox[j] : ow[j];
         const uint32_t dst = lds0 + st * kGemmStageBytes + (idx < 8 ? 0 : kGemmOpBytes) + j * 1024;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // the note that M0 is reserved
         asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                     :: "v"(off), "s"(base), "s"(dst) : "memory");
+                     :: "v"(off), "s"(base), "s"(dst) : "memory", "m0");
+#pragma clang diagnostic pop
     };
     auto fetch = [&](int kt, int st) {
 #pragma unroll
@@ -1209,7 +1329,7 @@ hipError_t launch_rope_cossin(const CosSinParams &params, hipStream_t stream)
     CosSinParams p = params;
     const uint32_t rows = p.vec_total / (uint32_t)(p.R / 8);
     const bool paired = p.R % 16 == 0;
-    const uint32_t per_row = paired ? (uint32_t)(p.R / 16) : (uint32_t)(p.R / kCosSinCols);
+    const uint32_t per_row = paired ? (uint32_t)(p.R / 16) : (uint32_t)(p.R / 8);
     p.vec_total = rows * per_row;
     p.div_vecs = make_fastdiv(per_row);
     uint32_t blocks = (p.vec_total + kThreads - 1) / kThreads;
@@ -1232,16 +1352,152 @@ hipError_t launch_rope_cossin_grid(const CosSinGridParams &p, hipStream_t stream
     return hipGetLastError();
 }
 
+// The cross-lane kernels take heads of 8..128 columns (D/8 a power of two,
+// so a head row sits in one 16-lane row of a wave) with a rotation, and
+// views of fewer than 2^31 vectors.
+static bool rope_xlane_fits(const RopeParams &p)
+{
+    const int dv = p.D / 8;
+    const int64_t vecs = p.tokens * p.H * dv;
+    return p.R >= 16 && p.D <= 128 && (dv & (dv - 1)) == 0 && vecs > 0 && vecs < ((int64_t)1 << 31);
+}
+
+// Token-linear views whose heads fill whole waves (rope_lean_kernel).
+static bool rope_lean_fits(const RopeParams &p)
+{
+    if (!rope_xlane_fits(p) || (p.H * (p.D / 8)) % 64 != 0)
+        return false;
+    const int64_t S = p.div_s.d, B = p.tokens / S;
+    for (int v = 0; v < p.n_views; ++v) {
+        const RopeView &V = p.v[v];
+        if (V.xs_h != p.D || V.os_h != p.D || V.xs_s >= ((int64_t)1 << 31) ||
+            V.os_s >= ((int64_t)1 << 31))
+            return false;
+        if (B > 1 && (V.xs_b != S * V.xs_s || V.os_b != S * V.os_s))
+            return false;
+    }
+    return true;
+}
+
+static int log2_vecs(int D)
+{
+    int l = 0;
+    while ((1 << l) < D / 8)
+        ++l;
+    return l;
+}
+
+static void *rope_lean_pick(int hv)
+{
+    switch (hv) {
+    case 1: return reinterpret_cast<void *>(rope_lean_kernel<1>);
+    case 2: return reinterpret_cast<void *>(rope_lean_kernel<2>);
+    case 3: return reinterpret_cast<void *>(rope_lean_kernel<3>);
+    case 4: return reinterpret_cast<void *>(rope_lean_kernel<4>);
+    case 5: return reinterpret_cast<void *>(rope_lean_kernel<5>);
+    case 6: return reinterpret_cast<void *>(rope_lean_kernel<6>);
+    case 7: return reinterpret_cast<void *>(rope_lean_kernel<7>);
+    default: return reinterpret_cast<void *>(rope_lean_kernel<8>);
+    }
+}
+
+template <int HV>
+static void *rope_xlane_pick(bool lines)
+{
+    return lines ? reinterpret_cast<void *>(rope_xlane_kernel<HV, 2, true>)
+                 : reinterpret_cast<void *>(rope_xlane_kernel<HV, 2, false>);
+}
+
+static void *rope_xlane_pick_hv(int hv, bool lines)
+{
+    switch (hv) {
+    case 1: return rope_xlane_pick<1>(lines);
+    case 2: return rope_xlane_pick<2>(lines);
+    case 3: return rope_xlane_pick<3>(lines);
+    case 4: return rope_xlane_pick<4>(lines);
+    case 5: return rope_xlane_pick<5>(lines);
+    case 6: return rope_xlane_pick<6>(lines);
+    case 7: return rope_xlane_pick<7>(lines);
+    default: return rope_xlane_pick<8>(lines);
+    }
+}
+
+// One launch per view group: rope_lean_kernel, 256 vectors per workgroup,
+// the views one after the other.
+static hipError_t launch_rope_lean(const RopeParams &params, hipStream_t stream)
+{
+    RopeParams p = params;
+    const int dv = p.D / 8;
+    p.log_vecs = log2_vecs(p.D);
+    p.vecs_per_view = (uint32_t)(p.tokens * p.H * dv);
+    p.div_vecs = make_fastdiv((uint32_t)(p.H * dv));
+    p.chunks = (uint32_t)(((int64_t)p.vecs_per_view + 255) / 256);
+    p.chunk0 = 0;
+    if ((int64_t)p.chunks * p.n_views >= ((int64_t)1 << 23))
+        return hipErrorInvalidValue;  // excluded by rope_xlane_fits (vectors < 2^31)
+    void *args[] = {&p};
+    hipError_t e = hipLaunchKernel(rope_lean_pick(p.R / 16), dim3(p.chunks * (uint32_t)p.n_views),
+                                   dim3(256), args, 0, stream);
+    return e == hipSuccess ? hipGetLastError() : e;
+}
+
+// rope_xlane_kernel: two vectors per lane, 256 lanes per workgroup.
+static hipError_t launch_rope_xlane(const RopeParams &params, hipStream_t stream)
+{
+    RopeParams p = params;
+    const int dv = p.D / 8;
+    p.log_vecs = log2_vecs(p.D);
+    p.vecs_per_view = (uint32_t)(p.tokens * p.H * dv);
+    p.div_views = make_fastdiv((uint32_t)p.n_views);
+    p.chunk_vecs = 512;
+    // Every wave instruction moves 64 consecutive vectors; they are whole
+    // contiguous 128-byte lines when a token's heads are contiguous, its
+    // vectors fill whole waves and rows start on line boundaries.
+    bool lines = (p.H * dv) % 64 == 0;
+    for (int v = 0; v < p.n_views; ++v) {
+        const RopeView &V = p.v[v];
+        lines = lines && V.xs_h == p.D && V.os_h == p.D && V.xs_s % 64 == 0 && V.os_s % 64 == 0 &&
+                V.xs_b % 64 == 0 && V.os_b % 64 == 0 && ((uintptr_t)V.x & 127) == 0 &&
+                ((uintptr_t)V.out & 127) == 0;
+    }
+    void *kernel = rope_xlane_pick_hv(p.R / 16, lines);
+    const int64_t chunks = ((int64_t)p.vecs_per_view + p.chunk_vecs - 1) / p.chunk_vecs;
+    const int64_t per_launch = kMaxRopeWorkgroups / p.n_views;
+    for (int64_t c0 = 0; c0 < chunks; c0 += per_launch) {
+        p.chunk0 = (uint32_t)c0;
+        const int64_t n = chunks - c0 < per_launch ? chunks - c0 : per_launch;
+        void *args[] = {&p};
+        hipError_t e = hipLaunchKernel(kernel, dim3((uint32_t)(n * p.n_views)), dim3(256), args, 0,
+                                       stream);
+        if (e == hipSuccess)
+            e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+static hipError_t launch_rope_items(const RopeParams &params, hipStream_t stream);
+
 hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
+{
+    if (rope_lean_fits(params))
+        return launch_rope_lean(params, stream);
+    if (rope_xlane_fits(params))
+        return launch_rope_xlane(params, stream);
+    return launch_rope_items(params, stream);
+}
+
+static hipError_t launch_rope_items(const RopeParams &params, hipStream_t stream)
 {
     RopeParams p = params;
     p.tok_per_wg = rope_tokens_per_workgroup(p.H, p.D, p.R);
     p.div_views = make_fastdiv((uint32_t)p.n_views);
-    size_t lds = RGG_ROPE_LDS ? (size_t)p.tok_per_wg * p.R * 2 * sizeof(float) : 0;
+    size_t lds = (size_t)p.tok_per_wg * p.R * 2 * sizeof(float);
     // One-token workgroups give each wave its own staged row unless the
     // copies would crowd LDS (wide rotations); then the workgroup shares one.
     const size_t wave_lds = (size_t)(kRopeBlock / 64) * p.R * 2 * sizeof(float);
-    p.wave_stage = RGG_ROPE_LDS && RGG_ROPE_WAVE_STAGE && p.tok_per_wg == 1 && wave_lds <= 65536;
+    p.wave_stage = p.tok_per_wg == 1 && wave_lds <= 65536;
     if (p.wave_stage)
         lds = wave_lds;
     // Whole lines per instruction when each half (R/2 bf16 = R bytes) and
@@ -1264,7 +1520,6 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
         kernel = rope_rotate_half_kernel<false, true>;
     else
         kernel = rope_rotate_half_kernel<false, false>;
-#if RGG_ROPE_LANE
     // When R/2 is not a whole number of 128-byte lines the two-vector items
     // split lines between store instructions; one contiguous vector per lane
     // keeps every line whole.
@@ -1282,7 +1537,6 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
             items = (int64_t)p.H * (p.D / 8);
         }
     }
-#endif
     // A one-token workgroup whose token needs k >= 2 whole passes hands them
     // to k workgroups instead (a partial last pass stays with the first).
     p.parts = p.tok_per_wg == 1 ? (int32_t)std::max<int64_t>(1, items / (kRopeBlock * kRopeUnroll))
@@ -1310,7 +1564,11 @@ hipError_t launch_rope_rotate_half(const RopeParams &params, hipStream_t stream)
 
 hipError_t launch_gelu_and_mul(const GegluParams &p, int grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL(gelu_and_mul_kernel, dim3(grid), dim3(kGegluBlock), 0, stream, p);
+    const bool lines = p.hidden % 512 == 0 && p.out_stride % 64 == 0 && ((uintptr_t)p.out & 127) == 0;
+    if (lines)
+        hipLaunchKernelGGL(gelu_and_mul_kernel<true>, dim3(grid), dim3(kGegluBlock), 0, stream, p);
+    else
+        hipLaunchKernelGGL(gelu_and_mul_kernel<false>, dim3(grid), dim3(kGegluBlock), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1359,7 +1617,6 @@ hipError_t launch_build_gelu_table(hipStream_t stream)
 
 int rope_tokens_per_workgroup(int H, int D, int R)
 {
-#if RGG_ROPE_TPW_FIT
     // Heads small enough that a token's work items fill under one
     // workgroup pass are grouped: the token count that fills the one or two
     // passes best (the fewest passes on a tie), with the fp32 cos/sin rows
@@ -1378,33 +1635,13 @@ int rope_tokens_per_workgroup(int H, int D, int R)
         }
     }
     return best;
-#else
-    // About RGG_ROPE_VEC_PER_WG 16-byte vectors of x per workgroup, with the
-    // fp32 cos/sin staging within 32 KiB of LDS.
-    int64_t vec_per_tok = (int64_t)H * (D / 8);
-    int64_t t = vec_per_tok > 0 ? RGG_ROPE_VEC_PER_WG / vec_per_tok : 64;
-    if (t < 1)
-        t = 1;
-    if (t > 64)
-        t = 64;
-    while (t > 1 && t * R * 8 > 32768)
-        --t;
-    return (int)t;
-#endif
 }
 
-int geglu_grid(uint32_t vec_total, int cu_count)
+int geglu_grid(uint32_t vec_total, int)
 {
-    // kGegluVec vectors per lane; with RGG_GEGLU_WG_PER_CU > 0 the grid is
-    // capped at that many workgroups per compute unit and each loops.
-    const uint32_t chunk = kGegluBlock * kGegluVec;
-    uint32_t chunks = (vec_total + chunk - 1) / chunk;
-    if (chunks == 0)
-        chunks = 1;
-    if (RGG_GEGLU_WG_PER_CU == 0)
-        return (int)chunks;
-    uint32_t cap = (uint32_t)(cu_count > 0 ? cu_count : 256) * RGG_GEGLU_WG_PER_CU;
-    return (int)(chunks < cap ? chunks : cap);
+    // one 16-byte vector per lane, one pass
+    const uint32_t blocks = (vec_total + kGegluBlock - 1) / kGegluBlock;
+    return (int)(blocks == 0 ? 1 : blocks);
 }
 
 }  // namespace rgg

@@ -56,7 +56,13 @@ struct RopeParams {
     FastDiv div_heads;     // divisor H
     FastDiv div_slots;     // divisor R/16: item -> (token-local, head, slot), no tail
     FastDiv div_slots_tail;  // divisor slots_tail
-    FastDiv div_vecs;      // divisor D/8: vector index -> (head, vector of the head row)
+    FastDiv div_vecs;      // divisor D/8: vector index -> (head, vector of the head row);
+                           // rope_lean_kernel: H * D/8, vector index -> (token, vector)
+    // cross-lane kernels (heads of at most 128 columns)
+    uint32_t vecs_per_view;  // tokens * H * D/8
+    int32_t log_vecs;        // log2(D/8)
+    int32_t chunk_vecs;      // vectors per workgroup (rope_xlane_kernel)
+    uint32_t chunks;         // workgroups per view (rope_lean_kernel)
 };
 
 struct CosSinParams {

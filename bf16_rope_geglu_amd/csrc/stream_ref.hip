@@ -5,7 +5,7 @@
 // method.
 //
 //   int rgg_stream_ref(const void *a, const void *b, void *out, int64_t n_vec,
-//                      int block, int vpl, int grid, int policy,
+//                      int block, int vpl, int grid, int policy, int lds,
 //                      hipStream_t stream);
 //
 // a == NULL, b == NULL: out[i] = i              (write only)
@@ -19,7 +19,9 @@
 //   grid  > 0: `grid` workgroups walk the chunks with a stride of `grid`,
 //              each loading its next chunk before storing the current one.
 // policy bit 0: nontemporal loads; bits 1-2: stores 0 plain, 1 nontemporal,
-// 2 write-through to the device coherence point (sc1), 3 both.
+// 2 write-through to the device coherence point (sc1), 3 both.  `lds` bytes
+// of (unused) LDS per workgroup cap how many workgroups share a compute unit
+// (160 KiB of LDS each): 0 leaves occupancy to the register count.
 // block is 64..1024 (a multiple of 64), vpl 1, 2, 4 or 8; all pointers are
 // device memory, 16-byte aligned.  Returns 0, 2 for bad arguments, 6 for a
 // launch error.
@@ -133,14 +135,14 @@ void *pick_vpl(int vpl, int policy)
 
 extern "C" __attribute__((visibility("default"))) int
 rgg_stream_ref(const void *a, const void *b, void *out, int64_t n_vec, int block_size, int vpl,
-               int grid, int policy, hipStream_t stream)
+               int grid, int policy, int lds, hipStream_t stream)
 {
     // Stores address the output through a buffer resource with 32-bit byte
     // offsets, so n_vec stays below 2^27 vectors (2 GiB).
     if (n_vec <= 0 || n_vec >= ((int64_t)1 << 27) || (b && !a) || !out ||
         ((uintptr_t)a | (uintptr_t)b | (uintptr_t)out) & 15 || block_size < 64 ||
         block_size > 1024 || block_size % 64 || (vpl != 1 && vpl != 2 && vpl != 4 && vpl != 8) ||
-        grid < 0 || policy < 0 || policy > 7)
+        grid < 0 || policy < 0 || policy > 7 || lds < 0 || lds > 65536)
         return 2;
     const int64_t chunk = (int64_t)block_size * vpl;
     const int64_t chunks = (n_vec + chunk - 1) / chunk;
@@ -152,7 +154,7 @@ rgg_stream_ref(const void *a, const void *b, void *out, int64_t n_vec, int block
     v4u *vo = static_cast<v4u *>(out);
     uint32_t n = (uint32_t)n_vec;
     void *args[] = {&va, &vb, &vo, &n};
-    hipError_t e = hipLaunchKernel(k, g, blk, args, 0, stream);
+    hipError_t e = hipLaunchKernel(k, g, blk, args, (size_t)lds, stream);
     if (e == hipSuccess)
         e = hipGetLastError();
     return e == hipSuccess ? 0 : 6;

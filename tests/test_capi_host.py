@@ -289,11 +289,21 @@ def test_stream_reference_loads_and_checks_arguments():
     import bench
 
     ref = bench.stream_ref_library()
-    assert ref.rgg_stream_ref(A, None, A + 4096, 0, 256, None) == 2
-    assert ref.rgg_stream_ref(A, None, A + 4096, 16, 96, None) == 2
-    assert ref.rgg_stream_ref(A + 8, None, A + 4096, 16, 256, None) == 2
-    assert ref.rgg_stream_ref(None, A, A + 4096, 16, 256, None) == 2
-    assert ref.rgg_stream_ref(A, None, None, 16, 256, None) == 2
+
+    def call(a=A, b=None, out=A + 4096, n=16, block=256, vpl=1, grid=0, policy=3, lds=0):
+        return ref.rgg_stream_ref(a, b, out, n, block, vpl, grid, policy, lds, None)
+
+    assert call(n=0) == 2
+    assert call(n=1 << 27) == 2                  # beyond the 32-bit byte offsets of the stores
+    assert call(block=96) == 2
+    assert call(block=2048) == 2
+    assert call(a=A + 8) == 2
+    assert call(a=None, b=A) == 2
+    assert call(out=None) == 2
+    assert call(vpl=3) == 2
+    assert call(grid=-1) == 2
+    assert call(policy=8) == 2
+    assert call(lds=65537) == 2
 
 
 def test_selfcheck_argument_checks(lib):
