@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(HERE, "lib")
 LIBRARY = os.path.join(LIBDIR, "librgg.so")
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "capi.cpp"),
-           os.path.join(CSRC, "selfcheck.cpp")]
+           os.path.join(CSRC, "selfcheck.cpp"), os.path.join(CSRC, "noalloc.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -16,6 +16,7 @@
 #include "launch.h"
 #include "layout.h"
 #include "rgg.h"
+#include "selfcheck.h"
 
 namespace {
 
@@ -446,6 +447,8 @@ int rgg_prepare_device(int device)
     if (hipSetDevice(device) != hipSuccess)
         return RGG_ERR_HIP;
     int st = ensure_table(device, nullptr);
+    if (st == RGG_OK)
+        st = rgg::noalloc_prepare(device);
     if (hipSetDevice(prev) != hipSuccess && st == RGG_OK)
         st = RGG_ERR_HIP;
     return st;

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include "rgg.h"
+#include "selfcheck.h"
 
 namespace {
 
@@ -44,6 +45,7 @@ constexpr size_t kUsed = kPpOut + kPm * 2 * kPh * 2;
 static_assert(kPx % 256 == 0 && kPw % 256 == 0 && kPfOut % 256 == 0 && kPpOut % 256 == 0,
               "projection operands 256-byte aligned");
 static_assert(kUsed <= RGG_SELFCHECK_WORKSPACE_BYTES, "workspace layout");
+static_assert(kUsed == rgg::kSelfcheckBytes, "staging size");
 
 // bit 0: cos/sin of fp32 angles, correctly rounded (50-digit evaluation).
 const uint32_t kAngles[8] = {0x00000000u, 0x80000000u, 0x40490FDBu, 0x3FC90FDBu,
@@ -119,16 +121,16 @@ uint16_t bf16_bits(float f)  // f exactly representable in bf16
 bool is_nan(uint16_t b) { return (b & 0x7F80u) == 0x7F80u && (b & 0x7Fu) != 0; }
 
 template <typename T>
-void put(std::vector<uint8_t> &img, size_t off, size_t i, T v)
+void put(uint8_t *img, size_t off, size_t i, T v)
 {
-    memcpy(img.data() + off + i * sizeof(T), &v, sizeof(T));
+    memcpy(img + off + i * sizeof(T), &v, sizeof(T));
 }
 
 template <typename T>
-T get(const std::vector<uint8_t> &img, size_t off, size_t i)
+T get(const uint8_t *img, size_t off, size_t i)
 {
     T v;
-    memcpy(&v, img.data() + off + i * sizeof(T), sizeof(T));
+    memcpy(&v, img + off + i * sizeof(T), sizeof(T));
     return v;
 }
 
@@ -143,25 +145,20 @@ uint16_t zero_angle_x(int i)
 
 }  // namespace
 
-extern "C" int rgg_selfcheck(void *workspace, int64_t workspace_bytes, hipStream_t stream,
-                             uint32_t *failed)
+int rgg::selfcheck_run(uint8_t *ws, hipStream_t stream, uint32_t checks, uint32_t *failed,
+                       uint8_t *in, uint8_t *out)
 {
     if (failed)
         *failed = 0;
-    if (!workspace)
-        return RGG_ERR_NULL;
-    if (workspace_bytes < RGG_SELFCHECK_WORKSPACE_BYTES)
-        return RGG_ERR_SHAPE;
-    if (reinterpret_cast<uintptr_t>(workspace) & 255)
-        return RGG_ERR_ALIGN;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cap) != hipSuccess)
         return RGG_ERR_HIP;
     if (cap != hipStreamCaptureStatusNone)
         return RGG_ERR_CAPTURING;
-
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    std::vector<uint8_t> in(kUsed, 0), out(kUsed, 0);
+    const bool c_tab = checks & 1u, c_ra = checks & 2u, c_rb = checks & 4u;
+    const bool c_ge = checks & (7u << 3), c_proj = checks & (1u << 6);
+    memset(in, 0, kUsed);
+    memset(out, 0, kUsed);
     for (int j = 0; j < 8; ++j)
         put<uint32_t>(in, kFreq, j, kAngles[j]);
     for (int j = 0; j < 8; ++j) {
@@ -194,34 +191,36 @@ extern "C" int rgg_selfcheck(void *workspace, int64_t workspace_bytes, hipStream
             put<uint16_t>(in, kPw, (size_t)(kPh + j) * kPk + m, proj_up(m, j));
         }
 
-    if (hipMemcpyAsync(ws, in.data(), kUsed, hipMemcpyHostToDevice, stream) != hipSuccess)
+    if (hipMemcpyAsync(ws, in, kUsed, hipMemcpyHostToDevice, stream) != hipSuccess)
         return RGG_ERR_HIP;
-    int st = rope_cossin_precompute(reinterpret_cast<const float *>(ws + kFreq), 1, 1, 8, 8, 8,
+    int st = RGG_OK;
+    if (c_tab)
+        st = rope_cossin_precompute(reinterpret_cast<const float *>(ws + kFreq), 1, 1, 8, 8, 8,
                                     reinterpret_cast<uint16_t *>(ws + kCsCos),
                                     reinterpret_cast<uint16_t *>(ws + kCsSin), stream);
     const rgg_rope_view va = {reinterpret_cast<const uint16_t *>(ws + kRaX),
                               reinterpret_cast<uint16_t *>(ws + kRaOut), 16, 16, 16, 16, 16, 16};
-    if (st == RGG_OK)
+    if (st == RGG_OK && c_ra)
         st = rope_rotate_half_bf16(&va, 1, 1, 1, 1, 16, 16,
                                    reinterpret_cast<const uint16_t *>(ws + kRaCos),
                                    reinterpret_cast<const uint16_t *>(ws + kRaSin), stream);
     const rgg_rope_view vb = {reinterpret_cast<const uint16_t *>(ws + kRbX),
                               reinterpret_cast<uint16_t *>(ws + kRbOut), 64, 64, 32, 64, 64, 32};
-    if (st == RGG_OK)
+    if (st == RGG_OK && c_rb)
         st = rope_rotate_half_bf16(&vb, 1, 1, 1, 2, 32, 16,
                                    reinterpret_cast<const uint16_t *>(ws + kRbCos),
                                    reinterpret_cast<const uint16_t *>(ws + kRbSin), stream);
-    if (st == RGG_OK)
+    if (st == RGG_OK && c_ge)
         st = gelu_and_mul_bf16(reinterpret_cast<const uint16_t *>(ws + kGe1In), 256, 256, 512,
                                reinterpret_cast<uint16_t *>(ws + kGe1Out), 256, stream);
-    if (st == RGG_OK)
+    if (st == RGG_OK && c_ge)
         st = gelu_and_mul_bf16(reinterpret_cast<const uint16_t *>(ws + kGe2In), 256, 256, 512,
                                reinterpret_cast<uint16_t *>(ws + kGe2Out), 256, stream);
-    if (st == RGG_OK)
+    if (st == RGG_OK && c_proj)
         st = gemm_geglu_bf16(reinterpret_cast<const uint16_t *>(ws + kPx), kPm, kPk, kPk,
                              reinterpret_cast<const uint16_t *>(ws + kPw), kPh, kPk,
                              reinterpret_cast<uint16_t *>(ws + kPfOut), kPh, stream);
-    if (st == RGG_OK)
+    if (st == RGG_OK && c_proj)
         st = gemm_bf16_nt(reinterpret_cast<const uint16_t *>(ws + kPx), kPm, kPk, kPk,
                           reinterpret_cast<const uint16_t *>(ws + kPw), 2 * kPh, kPk,
                           reinterpret_cast<uint16_t *>(ws + kPpOut), 2 * kPh, stream);
@@ -229,7 +228,7 @@ extern "C" int rgg_selfcheck(void *workspace, int64_t workspace_bytes, hipStream
         (void)hipStreamSynchronize(stream);
         return st;
     }
-    if (hipMemcpyAsync(out.data(), ws, kUsed, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+    if (hipMemcpyAsync(out, ws, kUsed, hipMemcpyDeviceToHost, stream) != hipSuccess ||
         hipStreamSynchronize(stream) != hipSuccess)
         return RGG_ERR_HIP;
 
@@ -312,7 +311,24 @@ extern "C" int rgg_selfcheck(void *workspace, int64_t workspace_bytes, hipStream
                 get<uint16_t>(out, kPpOut, (size_t)m * 2 * kPh + kPh + j) != up)
                 mask |= 1u << 6;
         }
+    mask &= checks;
     if (failed)
         *failed = mask;
     return mask ? RGG_ERR_SELFCHECK : RGG_OK;
+}
+
+extern "C" int rgg_selfcheck(void *workspace, int64_t workspace_bytes, hipStream_t stream,
+                             uint32_t *failed)
+{
+    if (failed)
+        *failed = 0;
+    if (!workspace)
+        return RGG_ERR_NULL;
+    if (workspace_bytes < RGG_SELFCHECK_WORKSPACE_BYTES)
+        return RGG_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255)
+        return RGG_ERR_ALIGN;
+    std::vector<uint8_t> in(kUsed), out(kUsed);
+    return rgg::selfcheck_run(static_cast<uint8_t *>(workspace), stream, RGG_SELFCHECK_ALL, failed,
+                              in.data(), out.data());
 }

@@ -264,8 +264,25 @@ RGG_API int rgg_prepare_device(int device);
  * are overwritten.
  */
 #define RGG_SELFCHECK_WORKSPACE_BYTES (1 << 20)
+#define RGG_SELFCHECK_ALL 0x7Fu   /* bits 0-6 */
 RGG_API int rgg_selfcheck(void *workspace, int64_t workspace_bytes, hipStream_t stream,
                           uint32_t *failed);
+
+/*
+ * The same self-check without a workspace, for callers that cannot allocate
+ * device memory (a serving loop's health check, a harness that forbids
+ * hipMalloc).  It runs the checks selected by `checks` (a nonzero subset of
+ * RGG_SELFCHECK_ALL: bit k runs check k of rgg_selfcheck; bits 3-5 share one
+ * GEGLU run) over a 1 MiB device array that the library holds for each GPU it
+ * runs on until the process ends, and host images it holds statically; it
+ * calls no allocating routine.  Returns and sets *failed exactly as
+ * rgg_selfcheck does for the selected bits, RGG_ERR_SHAPE for an empty or
+ * out-of-range mask, RGG_ERR_HIP if the array's device address cannot be
+ * looked up.  Synchronous; not allowed while `stream` is capturing.  Calls
+ * from several host threads are serialized by a lock; every call overwrites
+ * the array's staged region before it uses it.
+ */
+RGG_API int rgg_selfcheck_noalloc(uint32_t checks, hipStream_t stream, uint32_t *failed);
 
 /* Static, human-readable text for a status code (never NULL). */
 RGG_API const char *rgg_status_string(int status);

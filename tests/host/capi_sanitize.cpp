@@ -19,6 +19,7 @@
 
 #include "launch.h"
 #include "rgg.h"
+#include "selfcheck.h"
 
 // ---------------------------------------------------------------------------
 // stubs: the HIP runtime calls of the host layer, and the kernel launchers
@@ -95,6 +96,7 @@ hipError_t launch_build_gelu_table(hipStream_t)
     return hipSuccess;
 }
 int geglu_grid(uint32_t vec_total, int) { return (int)((vec_total + 511) / 512); }
+int noalloc_prepare(int) { return 0; }
 }  // namespace rgg
 
 // ---------------------------------------------------------------------------

@@ -42,7 +42,7 @@ def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert set(names) == {"rope_cossin_precompute", "rope_cossin_from_grid",
                           "rope_rotate_half_bf16", "gelu_and_mul_bf16", "gemm_bf16_nt",
-                          "gemm_geglu_bf16", "rgg_prepare_device", "rgg_selfcheck",
+                          "gemm_geglu_bf16", "rgg_prepare_device", "rgg_selfcheck", "rgg_selfcheck_noalloc",
                           "rgg_status_string"}
     for n in names:
         assert hasattr(lib, n), n
