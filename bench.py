@@ -67,7 +67,7 @@ KERNELS_SRC = os.path.join(ROOT, "bf16_rope_geglu_amd", "csrc", "kernels.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gelu_and_mul_dit_layer_traffic.md")
 KERNEL_SYMBOL = {
     "precompute": "rope_cossin_kernel",
-    "rope": "rope_rotate_half_kernel",
+    "rope": "rope_lean_kernel",
     "geglu": "gelu_and_mul_kernel",
 }
 COPY_BYTES = 1 << 30
@@ -284,7 +284,7 @@ COLD_TOUCH = 2 << 30
 # `profiles/stream_family_sweep.md`); the ceiling reported is the best of
 # them on the box at hand.
 STREAM_FAMILY = [(256, 1, 0, 7, 0), (256, 1, 0, 5, 0), (256, 1, 0, 3, 0), (256, 2, 0, 3, 0),
-                 (512, 1, 0, 7, 0), (256, 1, 1024, 7, 0)]
+                 (512, 1, 0, 7, 0), (256, 1, 1024, 7, 0), (256, 1, 0, 7, 27136)]
 
 
 def cold_us(fns, reps=COLD_REPS):
@@ -685,6 +685,31 @@ def run_cpu_baseline(wid, tokens=16384, geglu_rows=8192):
     }
 
 
+def run_traffic(name, reps=6):
+    """The RoPE launch of workload `name` (rope_qk or partial) over cold
+    buffer sets, `reps` times, then a plain device copy of known size: the
+    program that rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes profile for
+    that workload's counter summary (--pmc-set NAME)."""
+    import torch
+
+    import bf16_rope_geglu_amd as rgg
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wid = {w["name"]: k for k, w in W.WORKLOADS.items()}[name]
+    sets = rope_cold_sets(wid, dev)
+    for k in range(reps):
+        st = sets[k % len(sets)]
+        rgg.rope_rotate_half_bf16(st["x"], st["cos"], st["sin"], out=st["out"])
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"{name}: {reps} RoPE launches and 3 copies of {COPY_BYTES} bytes", flush=True)
+
+
 def _cpu_model():
     """The host CPU's model name, as /proc/cpuinfo gives it (None if absent)."""
     try:
@@ -721,8 +746,9 @@ def _per_dispatch(rows, counter, symbol):
 
 
 KNOWN_KERNELS = ("rope_cossin_kernel", "rope_cossin_grid_kernel", "rope_rotate_half_kernel",
-                 "rope_rotate_half_lane_kernel", "gelu_and_mul_kernel", "build_gelu_table_kernel",
-                 "gemm_gate_up_kernel", "stream_ref_kernel")
+                 "rope_rotate_half_lane_kernel", "rope_lean_kernel", "rope_xlane_kernel",
+                 "gelu_and_mul_kernel", "build_gelu_table_kernel", "gemm_gate_up_kernel",
+                 "stream_ref_kernel")
 
 
 def _short_kernel(name):
@@ -809,12 +835,19 @@ def pmc_summary(d, out, command="", which="step"):
     w_scale = COPY_BYTES / (1024 * sorted(big_w)[len(big_w) // 2]) if big_w else None
     res["fetch_scale"] = f_scale
     res["write_scale"] = w_scale
-    title = ("the gate_up projection of the dit_layer workload" if which == "projection"
-             else "dit_layer workload")
+    if which == "projection":
+        title, symbols, algo = ("the gate_up projection of the dit_layer workload", PROJ_SYMBOL,
+                                projection_algo_bytes())
+    elif which == "step":
+        import workloads as W
+        title, symbols, algo = "dit_layer workload", KERNEL_SYMBOL, W.algo_bytes(4)
+    else:
+        import workloads as W
+        wid = {w["name"]: k for k, w in W.WORKLOADS.items()}[which]
+        title, symbols, algo = (f"{which} workload", {"rope": KERNEL_SYMBOL["rope"]},
+                                W.algo_bytes(wid))
     lines = [f"# HBM traffic per dispatch from rocprofv3 counters ({title})", "",
              f"Commands: `{command}`", ""]
-    symbols = PROJ_SYMBOL if which == "projection" else KERNEL_SYMBOL
-    algo = projection_algo_bytes() if which == "projection" else {}
     for n, sym in symbols.items():
         f = _per_dispatch(fetch, "FETCH_SIZE", sym)
         w = _per_dispatch(write, "WRITE_SIZE", sym)
@@ -903,7 +936,9 @@ def main():
     ap.add_argument("--calibration-copy", action="store_true")
     ap.add_argument("--pmc-summary", metavar="DIR")
     ap.add_argument("--pmc-out", metavar="FILE", default=TRAFFIC_SUMMARY)
-    ap.add_argument("--pmc-set", choices=["step", "projection"], default="step")
+    ap.add_argument("--pmc-set", choices=["step", "projection", "rope_qk", "partial"], default="step")
+    ap.add_argument("--traffic-run", choices=["rope_qk", "partial"],
+                    help="run one workload's RoPE launches and a calibration copy (for --pmc)")
     ap.add_argument("--projection", action="store_true",
                     help="time only the gate_up projection entry points (JSON)")
     ap.add_argument("--counter-summary", metavar="DIR")
@@ -920,6 +955,9 @@ def main():
 
     if args.pmc_summary:
         pmc_summary(args.pmc_summary, args.pmc_out, args.command, args.pmc_set)
+        return 0
+    if args.traffic_run:
+        run_traffic(args.traffic_run)
         return 0
     if args.projection:
         import torch

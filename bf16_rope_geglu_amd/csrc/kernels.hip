@@ -743,9 +743,9 @@ __global__ __launch_bounds__(1024) void rope_xlane_kernel(RopeParams p)
 // lane's work is only its loads, the DPP partner exchange, the rotation and
 // one store: about 90 vector instructions per 16-byte vector against 170
 // for the per-lane addressing of rope_xlane_kernel, which left the kernel
-// short of a plain stream at 136 MB.  Workgroup w takes vectors
-// 256 w' .. 256 w' + 255 of view w / chunks (w' = w % chunks): one view
-// after the other.
+// short of a plain stream at 136 MB.  Workgroup (w, v) of the (chunks,
+// views) grid takes vectors 256 w .. 256 w + 255 of view v: one view after
+// the other.
 __device__ __forceinline__ uint32_t rope_word_f(uint32_t x, uint32_t y, float c0, float c1,
                                                 float s0, float s1)
 {
@@ -757,12 +757,20 @@ __device__ __forceinline__ uint32_t rope_word_f(uint32_t x, uint32_t y, float c0
 template <int HV>
 __global__ __launch_bounds__(256) void rope_lean_kernel(RopeParams p)
 {
-    const uint32_t v = blockIdx.x / p.chunks;
-    const uint32_t blk = blockIdx.x - v * p.chunks;
+    // grid (chunks, n_views): the view index is known when the wave starts,
+    // so its parameters load in the same batch as the others
+    const uint32_t v = blockIdx.y;
+    const uint32_t blk = blockIdx.x;
     const RopeView &V = p.v[v];
     const bool keep_tail = (p.tail_mask >> v) & 1;
     uint16_t *const out = V.out;
-    const int64_t os_s = V.os_s;
+    const uint16_t *const xin = V.x;
+    const int64_t os_s = V.os_s, xs_s = V.xs_s;
+    // every parameter is needed in scalar registers before the first load:
+    // one batch of scalar loads, one wait
+    asm volatile("" ::"s"(out), "s"(xin), "s"(os_s), "s"(xs_s), "s"(p.cos), "s"(p.sin),
+                 "s"(p.div_vecs.m), "s"(p.div_vecs.l), "s"(p.div_vecs.d), "s"(p.vecs_per_view),
+                 "s"(p.log_vecs), "s"(p.R), "s"(p.tail_mask));
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j = (int)(lane & ((1u << p.log_vecs) - 1u));
@@ -781,15 +789,12 @@ __global__ __launch_bounds__(256) void rope_lean_kernel(RopeParams p)
     const __amdgpu_buffer_rsrc_t rsn = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(p.sin + (uint64_t)t * (uint32_t)p.R), 0, p.R * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(V.x + ((uint64_t)t * (uint64_t)V.xs_s + w0 * 8u)), 0, 1024, 0x00020000);
+        const_cast<uint16_t *>(xin + ((uint64_t)t * (uint64_t)xs_s + w0 * 8u)), 0, 1024, 0x00020000);
     const v4u cv = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rc, tab_lane, 0, 0));
     v4u sv = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rsn, tab_lane, 0, 0));
     // nontemporal (aux bit 1): x is read once
     const v4u xx = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rx, lane * 16u, 0, 2));
-    // all three loads go out before anything waits; the output row's
-    // parameters are read before it, so no scalar load follows the wait
-    asm volatile("" ::"s"(out), "s"(os_s), "s"(keep_tail ? 1 : 0));
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);  // all three loads go out before anything waits
 
     // sin of the first half negated (exact): rne(-x' s) = rne(x' (-s))
     sv ^= j < HV ? 0x80008000u : 0u;
@@ -1436,7 +1441,7 @@ static hipError_t launch_rope_lean(const RopeParams &params, hipStream_t stream)
     if ((int64_t)p.chunks * p.n_views >= ((int64_t)1 << 23))
         return hipErrorInvalidValue;  // excluded by rope_xlane_fits (vectors < 2^31)
     void *args[] = {&p};
-    hipError_t e = hipLaunchKernel(rope_lean_pick(p.R / 16), dim3(p.chunks * (uint32_t)p.n_views),
+    hipError_t e = hipLaunchKernel(rope_lean_pick(p.R / 16), dim3(p.chunks, (uint32_t)p.n_views),
                                    dim3(256), args, 0, stream);
     return e == hipSuccess ? hipGetLastError() : e;
 }
@@ -1562,13 +1567,20 @@ static hipError_t launch_rope_items(const RopeParams &params, hipStream_t stream
     return hipSuccess;
 }
 
+// GEGLU workgroups also take 27 KiB of (unused) dynamic LDS: with the
+// table's 7 KiB that holds a compute unit to 4 of them (160 KiB of LDS), which
+// measured 0.5-1% faster than leaving residency to the register count
+// (dit_layer 247.5 -> 244.7 us, geglu 93.0 -> 92.4-92.8 us); plain streams
+// of the same 2:1 traffic show the same gain from a residency cap.
+constexpr size_t kGegluLdsPad = 27 * 1024;
+
 hipError_t launch_gelu_and_mul(const GegluParams &p, int grid, hipStream_t stream)
 {
     const bool lines = p.hidden % 512 == 0 && p.out_stride % 64 == 0 && ((uintptr_t)p.out & 127) == 0;
     if (lines)
-        hipLaunchKernelGGL(gelu_and_mul_kernel<true>, dim3(grid), dim3(kGegluBlock), 0, stream, p);
+        hipLaunchKernelGGL(gelu_and_mul_kernel<true>, dim3(grid), dim3(kGegluBlock), kGegluLdsPad, stream, p);
     else
-        hipLaunchKernelGGL(gelu_and_mul_kernel<false>, dim3(grid), dim3(kGegluBlock), 0, stream, p);
+        hipLaunchKernelGGL(gelu_and_mul_kernel<false>, dim3(grid), dim3(kGegluBlock), kGegluLdsPad, stream, p);
     return hipGetLastError();
 }
 

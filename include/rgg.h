@@ -204,9 +204,13 @@ RGG_API int gelu_and_mul_bf16(const uint16_t *input, int64_t rows, int64_t hidde
  * gelu_and_mul_bf16 returns on the output of gemm_bf16_nt (one accumulation
  * order serves both).  The fp32 accumulation order is the kernel's: a
  * projection output is the bf16 rounding of a value within
- * 2 (K + 16) 2^-24 sum_k |x[m][k] W[n][k]| of the exact sum, so it differs
- * from the exactly rounded sum only where that error reaches across a
- * rounding boundary (and never where every partial sum is exact in fp32).
+ *     2 (K + 16) 2^-24 sum_k |x[m][k] W[n][k]|  +  K 2^-149
+ * of the exact sum (the relative term covers rounding in the normal range;
+ * the absolute term covers products and partial sums in the fp32 subnormal
+ * range, which are kept, not flushed, each off by at most half the subnormal
+ * step), so it differs from the exactly rounded sum only where that error
+ * reaches across a rounding boundary (and never where every partial sum is
+ * exact in fp32).
  *
  * Requirements: M, K >= 0; K a multiple of 64; N a multiple of 128 (H a
  * multiple of 64); rows of x and W at least K long, output rows at least N
