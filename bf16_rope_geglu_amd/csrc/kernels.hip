@@ -144,6 +144,11 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
     const uint32_t nvec_row = p.div_vecs.d;
     const uint32_t S = p.div_s.d;
     const int half = p.R / 2;
+    // every parameter in scalar registers before the first load: one batch
+    // of scalar loads, one wait
+    asm volatile("" ::"s"(p.freqs), "s"(p.cos), "s"(p.sin), "s"(p.stride_s), "s"(p.stride_b),
+                 "s"(p.vec_total), "s"(p.div_vecs.m), "s"(p.div_vecs.l), "s"(nvec_row),
+                 "s"(p.div_s.m), "s"(p.div_s.l), "s"(S), "s"(p.R), "s"(gridDim.x));
     for (uint32_t idx = blockIdx.x * kThreads + threadIdx.x; idx < p.vec_total;
          idx += gridDim.x * kThreads) {
         uint32_t row = fdiv(idx, p.div_vecs);
@@ -362,13 +367,6 @@ __device__ __forceinline__ RopeItem rope_locate(const RopeParams &p, const RopeV
 
 constexpr int kRopeBlock = 256;
 constexpr int64_t kMaxRopeWorkgroups = (int64_t)1 << 20;  // per launch (2^28 work-items)
-
-__device__ __forceinline__ void load_bf16x8_as_f32(const uint16_t *src, float *dst)
-{
-    v4u w = *reinterpret_cast<const v4u *>(src);
-    dst[0] = bf_lo(w.x); dst[1] = bf_hi(w.x); dst[2] = bf_lo(w.y); dst[3] = bf_hi(w.y);
-    dst[4] = bf_lo(w.z); dst[5] = bf_hi(w.z); dst[6] = bf_lo(w.w); dst[7] = bf_hi(w.w);
-}
 
 constexpr int kRopeUnroll = 1;  // items per lane with their loads issued together
 
@@ -717,16 +715,16 @@ struct XlaneState {
     }
 };
 
-// One pass: workgroup w takes chunk w / n_views of view w % n_views.
+// One pass over a (chunks, views) grid: workgroup (w, v) takes chunk w of
+// view v; the view index is known when the wave starts, so all parameters
+// arrive in one batch of scalar loads.
 template <int HV, int VPL, bool Lines>
 __global__ __launch_bounds__(1024) void rope_xlane_kernel(RopeParams p)
 {
-    const uint32_t wg = blockIdx.x;
-    const uint32_t chunk = fdiv(wg, p.div_views);
-    const int v = (int)(wg - chunk * (uint32_t)p.n_views);
+    const int v = (int)blockIdx.y;
     const RopeView V = p.v[v];
     XlaneState<HV, VPL, Lines> st;
-    st.fetch(p, V, p.chunk0 + chunk);
+    st.fetch(p, V, blockIdx.x);
     __builtin_amdgcn_sched_barrier(0);  // every load goes out before anything waits
     st.finish(V, (p.tail_mask >> v) & 1);
 }
@@ -1453,7 +1451,6 @@ static hipError_t launch_rope_xlane(const RopeParams &params, hipStream_t stream
     const int dv = p.D / 8;
     p.log_vecs = log2_vecs(p.D);
     p.vecs_per_view = (uint32_t)(p.tokens * p.H * dv);
-    p.div_views = make_fastdiv((uint32_t)p.n_views);
     p.chunk_vecs = 512;
     // Every wave instruction moves 64 consecutive vectors; they are whole
     // contiguous 128-byte lines when a token's heads are contiguous, its
@@ -1466,20 +1463,13 @@ static hipError_t launch_rope_xlane(const RopeParams &params, hipStream_t stream
                 ((uintptr_t)V.out & 127) == 0;
     }
     void *kernel = rope_xlane_pick_hv(p.R / 16, lines);
-    const int64_t chunks = ((int64_t)p.vecs_per_view + p.chunk_vecs - 1) / p.chunk_vecs;
-    const int64_t per_launch = kMaxRopeWorkgroups / p.n_views;
-    for (int64_t c0 = 0; c0 < chunks; c0 += per_launch) {
-        p.chunk0 = (uint32_t)c0;
-        const int64_t n = chunks - c0 < per_launch ? chunks - c0 : per_launch;
-        void *args[] = {&p};
-        hipError_t e = hipLaunchKernel(kernel, dim3((uint32_t)(n * p.n_views)), dim3(256), args, 0,
-                                       stream);
-        if (e == hipSuccess)
-            e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
-    return hipSuccess;
+    // fewer than 2^31 vectors per view: fewer than 2^22 chunks of 512
+    const uint32_t chunks = (uint32_t)(((int64_t)p.vecs_per_view + p.chunk_vecs - 1) / p.chunk_vecs);
+    p.chunk0 = 0;
+    void *args[] = {&p};
+    hipError_t e = hipLaunchKernel(kernel, dim3(chunks, (uint32_t)p.n_views), dim3(256), args, 0,
+                                   stream);
+    return e == hipSuccess ? hipGetLastError() : e;
 }
 
 static hipError_t launch_rope_items(const RopeParams &params, hipStream_t stream);
