@@ -74,8 +74,15 @@ COPY_BYTES = 1 << 30
 
 
 def source_digest():
-    with open(KERNELS_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace are dropped,
+    so counters stay current across comment-only edits and go stale with any
+    change to the code itself."""
+    with open(KERNELS_SRC) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------

@@ -1452,13 +1452,20 @@ static hipError_t launch_rope_xlane(const RopeParams &params, hipStream_t stream
     p.log_vecs = log2_vecs(p.D);
     p.vecs_per_view = (uint32_t)(p.tokens * p.H * dv);
     p.chunk_vecs = 512;
-    // Every wave instruction moves 64 consecutive vectors; they are whole
-    // contiguous 128-byte lines when a token's heads are contiguous, its
-    // vectors fill whole waves and rows start on line boundaries.
-    bool lines = (p.H * dv) % 64 == 0;
+    // Streaming stores (store16_lines) address a wave's 64 vectors from its
+    // first live lane, so every wave must lie in one token (a token's
+    // vectors fill whole waves) with its output offsets rising with the
+    // lane (head rows in order, os_h >= D) inside a 1 GiB span (the wave's
+    // 64 / (D/8) head rows); they pay off when every head row is whole
+    // 128-byte lines on line boundaries, in the input too.  The (B, H, S, D)
+    // attention layout qualifies: a wave's head rows are far apart, but
+    // each is whole lines.
+    const int64_t wave_heads = 64 / dv;
+    bool lines = (p.H * dv) % 64 == 0 && p.D % 64 == 0;
     for (int v = 0; v < p.n_views; ++v) {
         const RopeView &V = p.v[v];
-        lines = lines && V.xs_h == p.D && V.os_h == p.D && V.xs_s % 64 == 0 && V.os_s % 64 == 0 &&
+        lines = lines && V.os_h >= p.D && (wave_heads - 1) * V.os_h + p.D < ((int64_t)1 << 29) &&
+                V.xs_h % 64 == 0 && V.os_h % 64 == 0 && V.xs_s % 64 == 0 && V.os_s % 64 == 0 &&
                 V.xs_b % 64 == 0 && V.os_b % 64 == 0 && ((uintptr_t)V.x & 127) == 0 &&
                 ((uintptr_t)V.out & 127) == 0;
     }

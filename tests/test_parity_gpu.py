@@ -966,11 +966,17 @@ def test_gemm_several_tiles_per_workgroup(orc, K):
 # layouts, limits, graphs
 # ---------------------------------------------------------------------------
 
-def test_rope_into_attention_layout(orc):
+@pytest.mark.parametrize("shape", [(2, 40, 6, 64, 64), (2, 37, 8, 64, 32), (1, 50, 16, 128, 128),
+                                   (2, 19, 4, 128, 96)],
+                         ids=["H6D64", "H8D64R32", "H16D128", "H4D128R96"])
+def test_rope_into_attention_layout(orc, shape):
     """Outputs written straight into a (B, H, S, D) buffer (the layout an
-    attention kernel reads) through output strides, q and k in one launch."""
-    B, S, H, D, R = 2, 40, 6, 64, 64
-    say("rope into (B,H,S,D) outputs")
+    attention kernel reads) through output strides, q and k in one launch:
+    a token whose vectors do not fill whole waves (H6D64), and tokens that
+    do (the streaming-store path, rotary parts with and without a tail, the
+    last workgroup partly past the end)."""
+    B, S, H, D, R = shape
+    say(f"rope into (B,H,S,D) outputs {shape}")
     q = W.normal_bf16((B, S, H, D), 8401)
     k = W.normal_bf16((B, S, H, D), 8402)
     cos, sin = orc.rope_cossin(W.freqs_unpaired(S, B, R, 8403))
