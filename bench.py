@@ -20,17 +20,28 @@ epilogue, the plain projection, the unfused pair, and the platform library
 GEMM followed by gelu_and_mul_bf16 for comparison (TFLOP/s against the
 2.5 PFLOP/s dense bf16 peak).  It is outside the step and its `value`.
 
+`configs` holds every graded kernel on every workload that has it (RoPE on
+rope_qk, partial and dit_layer; GEGLU on geglu and dit_layer), timed with
+cold caches (a HIP graph of launches over rotating buffer sets touching at
+least 2 GiB), each beside the fastest member of a family of plain streaming
+kernels moving the same bytes (STREAM_FAMILY, timed the same way on the same
+box) and its fraction of that ceiling (`vs_ceiling`).
+
 `cpu_baseline` times the CPU oracle on a bounded sample of the same
 workload (16384 tokens, 8192 GEGLU rows): `value` on one thread, and
 `all_cores` with the sample split over every core the process may use;
 `cpu` names the host CPU model.  `roofline.traffic` comes from the committed rocprofv3
-counter summary for the dominant kernel, and is null if the kernel source has
-changed since the counters were taken.
+counter summary for the dominant kernel, and is null if the kernel source's
+code (comments aside) has changed since the counters were taken.
 
     python bench.py --pmc-summary DIR --pmc-out FILE
 turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs (DIR/fetch, DIR/write)
 into that summary; --calibration-copy adds a plain device copy of known size
 to each step so the same runs calibrate the counters.
+
+    python bench.py --traffic-run rope_qk|partial
+runs only the RoPE kernel on that workload (and the calibration copy), for
+the same two counter passes; --pmc-set rope_qk|partial summarises them.
 
     python bench.py --projection [--calibration-copy]
 times only the gate_up projection entry points (and adds the calibration
@@ -47,6 +58,11 @@ prints a markdown table of every kernel on every workload with cold caches
 (bf16_rope_geglu_amd/lib/libstreamref.so) moving the same bytes with the
 same read:write ratio (write-only for the tables built from grid
 positions): the practical ceiling for that traffic.
+
+    python bench.py --stream-sweep [--stream-sweep-out FILE]
+times the whole streaming family (workgroup size, vectors per lane, one pass
+or persistent grids, load and store cache policies, residency caps) at each
+graded size and writes the ranking as markdown.
 """
 import argparse
 import csv
