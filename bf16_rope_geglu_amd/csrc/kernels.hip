@@ -964,7 +964,7 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
 // ---------------------------------------------------------------------------
 // GEGLU as the epilogue of the gate_up projection      [ERNIE-fuse §3]
 //
-// out = x W^T on the matrix cores (v_mfma_f32_32x32x16_bf16, fp32
+// out = x W^T on the matrix cores (v_mfma_f32_16x16x32_bf16, fp32
 // accumulation), the eager bf16 rounding of the projection applied to each
 // accumulator, then either stored or turned into up * G(gate) in the
 // epilogue, so the (M, 2H) intermediate never goes to memory.
@@ -975,10 +975,10 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
 // matching up rows of W in LDS.  Wave (wm, wn) owns rows wm*128 .. +127 and
 // columns wn*64 .. +63 of both the gate and the up block, so one lane holds
 // the gate and the up accumulator of the same (row, column).  W is the
-// first MFMA operand and x the second, so in a 32x32 block lane l holds
-// output row l % 32 and, in its accumulators v, output columns
-// (v / 4) * 8 + (l / 32) * 4 + v % 4.  Operands: lane l supplies row l % 32
-// of W or of x and the 8 consecutive k at (l / 32) * 8 of a 16-wide step.
+// first MFMA operand and x the second; in a 16x16 block lane l holds output
+// row l % 16 and, in its four accumulators, output columns 4 (l / 16) .. +3.
+// Operands: lane l supplies row l % 16 of a 16-row block of W or of x and
+// the 8 consecutive k at 8 (l / 16) of a 32-wide step.
 //
 // Staging uses the direct global-to-LDS load (16 bytes per lane, one 1 KiB
 // run of LDS per instruction: 8 rows of 128 bytes), so the slices never pass
@@ -990,14 +990,17 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
 // stages of 64 KiB: slice kt + 1 is loaded into one while slice kt is read
 // from the other.
 //
-// Per slice each wave issues 64 products in 4 steps of 16 (one register
-// set of fragments per step, alternating).  The fragment reads of the next
-// step ride on the first 8 products of each step; the 16 loads of the next
-// slice go out two per three products over the first 24.  After 15
-// products of step 3 the wave waits for its own loads of the next slice
-// (loads complete in order) and passes the barrier that publishes them and
-// frees the stage just read; the last product carries the next slice's
-// step-0 reads.  A late barrier gives the loads the most time to arrive.
+// Per slice each wave issues 128 products in 2 steps of 64, product
+// (jb, ib) = (x block, W block) at 8 jb + ib.  The 8 W fragments of a step
+// stay in registers for the whole step (two sets, alternating); the x
+// fragments stream through a ring of four, each read 16 products before its
+// first use.  Step 0 issues the 16 loads of the next slice, one per three
+// products, and reads step 1's W fragments.  The last read of the current
+// stage is at product 40 of step 1; at product 48 the wave waits for its
+// loads and its reads, and passes the barrier that publishes the next slice
+// and frees this one; the next slice's W fragments and first x fragments
+// are read over the remaining 16 products, so its first products find them
+// in registers.
 //
 // Workgroups go to the 8 XCDs round robin; the block index is remapped so
 // that each XCD gets one contiguous run of tiles, and the run is walked in
@@ -1005,7 +1008,7 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
 // at one time share rows of x and of W in its L2.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmBM = 256;              // rows of x per workgroup
 constexpr int kGemmBN = 128;              // gate (and up) columns per workgroup
@@ -1017,7 +1020,13 @@ constexpr int kGemmStageBytes = 2 * kGemmOpBytes;
 constexpr size_t kGemmLds = kGemmLutBytes + kGemmStages * kGemmStageBytes;
 constexpr uint32_t kGemmGroupM = 8;
 constexpr int kGemmThreads = 256;
-constexpr int kGemmBarrierAt = 15;        // products of the last step before the barrier
+constexpr int kGemmBarrierAt = 48;        // product of step 1 that the barrier precedes
+constexpr int kGemmLoadEvery = 3;         // step 0 issues one load per this many products
+// The barrier must follow the last read of the current stage (the x block
+// read at product 40 of step 1) and precede the first read of the next one
+// (product 48); the loads stay in step 0.
+static_assert(kGemmBarrierAt > 40 && kGemmBarrierAt <= 48, "barrier between the two stages' reads");
+static_assert(16 * kGemmLoadEvery <= 64, "the next slice's loads go out in step 0");
 static_assert(kGemmLds <= 160 * 1024, "LDS of one CU");
 static_assert(kGemmLutBytes % 1024 == 0, "stages start on a 1 KiB boundary");
 static_assert(4 * 128 * 64 * 2 <= kGemmStageBytes, "epilogue blocks fit stage 1");
@@ -1126,32 +1135,34 @@ void gemm_gate_up_kernel(GemmParams p)
             dma1(kt, st, idx);
     };
 
-    f32x16 acc[4][4];  // [x row block][gate 0, gate 1, up 0, up 1]
+    f32x4 acc[8][8];  // [x row block of 16][W block of 16: gate 0..3, up 0..3]
 
-    // Operand fragments of one k16 step, double buffered in registers (set
-    // 0 / set 1): 4 of x, then gate 0, gate 1, up 0, up 1 of W.
-    const int ra = (wm * 128 + (lane & 31)) * 128;
-    const int rb = (wn * 64 + (lane & 31)) * 128;
-    bf16x8 fa[2][4], fb[2][4];
-    auto frag1 = [&](int st, int ks, int set, int idx) {
-        const uint8_t *sx = gsm + kGemmLutBytes + st * kGemmStageBytes;
-        const int ch = ((2 * ks + (lane >> 5)) ^ (((lane & 31) >> 1) & 7)) * 16;
-        if (idx < 4)
-            fa[set][idx] = *reinterpret_cast<const bf16x8 *>(sx + ra + idx * 32 * 128 + ch);
-        else
-            fb[set][idx - 4] = *reinterpret_cast<const bf16x8 *>(
-                sx + kGemmOpBytes + rb + (((idx - 4) >> 1) * kGemmBN + ((idx - 4) & 1) * 32) * 128 + ch);
+    // 16x16x32 products: lane l supplies row l % 16 of a 16-row block of W
+    // (first operand) or of x (second) and the 8 k at 8 (l / 16) of the
+    // 32-wide step; its 4 accumulators of a block are output row l % 16,
+    // columns 4 (l / 16) .. +3.  The row's swizzle (r / 2) % 8 depends only
+    // on l % 16 (blocks start on multiples of 16 rows).
+    const int sw = (lane & 15) >> 1;
+    const uint32_t lrow = (uint32_t)(lane & 15) * 128u;
+    const uint32_t koff0 = lrow + (uint32_t)(((lane >> 4) ^ sw) << 4);
+    const uint32_t koff1 = lrow + (uint32_t)(((4 + (lane >> 4)) ^ sw) << 4);
+    const uint32_t xrow0 = (uint32_t)(wm * 128) * 128u;
+    const uint32_t wrow0 = (uint32_t)kGemmOpBytes + (uint32_t)(wn * 64) * 128u;
+    bf16x8 wf[2][8];  // W fragments of a step, double buffered
+    bf16x8 xf[4];     // x fragments, a ring of four
+    auto wread = [&](int st, int s, int set, int ib) {
+        const uint8_t *b = gsm + kGemmLutBytes + st * kGemmStageBytes + wrow0 +
+                           (ib < 4 ? ib * 2048 : 128 * 128 + (ib - 4) * 2048);
+        wf[set][ib] = *reinterpret_cast<const bf16x8 *>(b + (s ? koff1 : koff0));
     };
-    // Fragments are read in the order the products first use them.
-    constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
-    auto mma1 = [&](int set, int idx) {
-        const int i = idx >> 2, j = idx & 3;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
+    auto xread = [&](int st, int s, int jb) {
+        const uint8_t *b = gsm + kGemmLutBytes + st * kGemmStageBytes + xrow0 + jb * 2048;
+        xf[jb & 3] = *reinterpret_cast<const bf16x8 *>(b + (s ? koff1 : koff0));
+    };
+    auto mma1 = [&](int set, int jb, int ib) {
+        acc[jb][ib] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[set][ib], xf[jb & 3], acc[jb][ib], 0, 0, 0);
     };
 
-    // The workgroup walks tiles blockIdx.x, + gridDim.x, ... (one workgroup
-    // per CU).  The first slice of the next tile is requested before the
-    // epilogue of the current one, so its latency hides under it.
     const int KT = p.K / kGemmBK;
     uint32_t tile = blockIdx.x;
     int64_t m0;
@@ -1165,50 +1176,57 @@ void gemm_gate_up_kernel(GemmParams p)
     __syncthreads();
     for (;;) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 8; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    acc[a][b][v] = 0.0f;
+            for (int b = 0; b < 8; ++b)
+                acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-        // One slice: product pp = 16 * step + k in the order fixed by
-        // scheduling fences, each followed by at most a fragment read and a
-        // load (the product after the barrier carries the next slice's
-        // reads).  The last slice of a tile loads nothing and passes no
-        // barrier.
+        // One slice: two 32-wide steps of 64 products, product (jb, ib) at
+        // 8 jb + ib.  Step 0 carries the 16 loads of the next slice (one per
+        // three products) and the reads of step 1's W fragments; x fragments
+        // are read two blocks (16 products) ahead.  In step 1, at product 48
+        // the wave waits for its loads and its reads and passes the barrier
+        // that publishes the next slice and frees this one; the next slice's
+        // W fragments and first two x fragments follow.
         auto slice = [&](int kt, bool last) {
             const int st = kt & 1, sn = st ^ 1;
 #pragma unroll
-            for (int pp = 0; pp < 64; ++pp) {
-                const int step = pp >> 4, k = pp & 15;
-                if (step == 3 && k == kGemmBarrierAt && !last) {
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    __builtin_amdgcn_s_barrier();
+            for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                for (int pp = 0; pp < 64; ++pp) {
+                    const int jb = pp >> 3, ib = pp & 7;
+                    if (s == 1 && pp == kGemmBarrierAt && !last) {
+                        asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)" ::: "memory");
+                        __builtin_amdgcn_s_barrier();
+                        RGG_FENCE();
+                    }
+                    mma1(s, jb, ib);
+                    // x fragments: block jb + 2 of this step, or blocks 0, 1
+                    // of the next step (of the next slice after step 1)
+                    if (ib == 0) {
+                        if (jb < 6)
+                            xread(st, s, jb + 2);
+                        else if (s == 0)
+                            xread(st, 1, jb - 6);
+                        else if (!last)
+                            xread(sn, 0, jb - 6);
+                    }
+                    if (s == 0 && pp >= 8 && pp < 16)
+                        wread(st, 1, 1, pp - 8);
+                    if (s == 1 && pp >= kGemmBarrierAt && pp < kGemmBarrierAt + 8 && !last)
+                        wread(sn, 0, 0, pp - kGemmBarrierAt);
+                    if (s == 0 && !last && pp < 16 * kGemmLoadEvery && pp % kGemmLoadEvery == 0)
+                        dma1(kt + 1, sn, pp / kGemmLoadEvery);
                     RGG_FENCE();
                 }
-                mma1(step & 1, k);
-                if (step < 3 && k < 8)
-                    frag1(st, step + 1, (step + 1) & 1, kOrder[k]);
-                if (step == 3 && k >= kGemmBarrierAt && !last) {
-                    constexpr int nr = 16 - kGemmBarrierAt;
-                    constexpr int per = (8 + nr - 1) / nr;
-#pragma unroll
-                    for (int r = 0; r < per; ++r) {
-                        const int idx = (k - kGemmBarrierAt) * per + r;
-                        if (idx < 8)
-                            frag1(sn, 0, 0, kOrder[idx]);
-                    }
-                }
-                if (!last && pp < 24 && pp % 3 != 2)
-                    dma1(kt + 1, sn, pp / 3 * 2 + pp % 3);
-                RGG_FENCE();
             }
         };
         if (KT > 0) {
 #pragma unroll
-            for (int idx = 0; idx < 8; ++idx)
-                frag1(0, 0, 0, kOrder[idx]);
+            for (int ib = 0; ib < 8; ++ib)
+                wread(0, 0, 0, ib);
+            xread(0, 0, 0);
+            xread(0, 0, 1);
             RGG_FENCE();
             for (int kt = 0; kt + 1 < KT; ++kt)
                 slice(kt, false);
@@ -1228,15 +1246,10 @@ void gemm_gate_up_kernel(GemmParams p)
                 fetch(0, 0);
         }
 
-        // Epilogue: round each accumulator to bf16 (the projection's
-        // output), then keep it, or form rne(up * G(gate)).  Each wave writes
-        // its 128 x 64 block of results to its 16 KiB of stage 1 as
-        // 128-byte rows (16-byte chunk c of row r at chunk c ^ (r % 8); four
-        // adjacent columns per 8-byte write), then reads it back as 16-byte
-        // vectors, eight lanes per row, for whole-line global stores.  The
-        // plain product does this twice: gate columns, then up columns (H
-        // further along the row).  H is a multiple of 64, so a wave's block
-        // is wholly inside [0, H) or outside.
+        // Epilogue: round each accumulator to bf16, then keep it or form
+        // rne(up * G(gate)); the wave's 128 x 64 block goes through its
+        // 16 KiB of stage 1 (128-byte rows, chunk c of row r at c ^ (r % 8),
+        // 8 bytes = 4 columns per lane write) and out as 16-byte vectors.
         const uint16_t *lut = reinterpret_cast<const uint16_t *>(gsm);
         uint8_t *ep = gsm + kGemmLutBytes + kGemmStageBytes + wave * 16384;
         int el = lane;
@@ -1247,50 +1260,44 @@ void gemm_gate_up_kernel(GemmParams p)
         if (Geglu) {
             bool general = false;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int jb = 0; jb < 8; ++jb)
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
+                for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        general |= (bf16_of(acc[i][cb][v]) & 0x7FFFu) - 0x0100u >= kLutHi - 0x0100u;
+                    for (int v = 0; v < 4; ++v)
+                        general |= (bf16_of(acc[jb][ib][v]) & 0x7FFFu) - 0x0100u >= kLutHi - 0x0100u;
             anyg = __builtin_amdgcn_ballot_w64(general) != 0;
         }
 #pragma unroll
         for (int half = 0; half < (Geglu ? 1 : 2); ++half) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int jb = 0; jb < 8; ++jb) {
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb) {
-                    float G[16];
+                for (int ib = 0; ib < 4; ++ib) {
+                    uint32_t w0, w1;
                     if (Geglu) {
+                        float G[4];
                         if (!anyg) {
 #pragma unroll
-                            for (int v = 0; v < 16; ++v)
-                                G[v] = __uint_as_float(gelu_common(bf16_of(acc[i][cb][v]), lut));
+                            for (int v = 0; v < 4; ++v)
+                                G[v] = __uint_as_float(gelu_common(bf16_of(acc[jb][ib][v]), lut));
                         } else {
 #pragma unroll
-                            for (int v = 0; v < 16; ++v)
-                                G[v] = __uint_as_float(gelu_general(bf16_of(acc[i][cb][v]), lut) << 16);
+                            for (int v = 0; v < 4; ++v)
+                                G[v] = __uint_as_float(gelu_general(bf16_of(acc[jb][ib][v]), lut) << 16);
                         }
+                        const f32x4 &u = acc[jb][ib + 4];
+                        w0 = rne_pack(bf_lo(bf16_of(u[0])) * G[0], bf_lo(bf16_of(u[1])) * G[1]);
+                        w1 = rne_pack(bf_lo(bf16_of(u[2])) * G[2], bf_lo(bf16_of(u[3])) * G[3]);
+                    } else {
+                        const f32x4 &a = acc[jb][ib + 4 * half];
+                        w0 = rne_pack(a[0], a[1]);
+                        w1 = rne_pack(a[2], a[3]);
                     }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        uint32_t w0, w1;
-                        if (Geglu) {
-                            const f32x16 &u = acc[i][2 + cb];
-                            w0 = rne_pack(bf_lo(bf16_of(u[q * 4 + 0])) * G[q * 4 + 0],
-                                          bf_lo(bf16_of(u[q * 4 + 1])) * G[q * 4 + 1]);
-                            w1 = rne_pack(bf_lo(bf16_of(u[q * 4 + 2])) * G[q * 4 + 2],
-                                          bf_lo(bf16_of(u[q * 4 + 3])) * G[q * 4 + 3]);
-                        } else {
-                            const f32x16 &a = acc[i][2 * half + cb];
-                            w0 = rne_pack(a[q * 4 + 0], a[q * 4 + 1]);
-                            w1 = rne_pack(a[q * 4 + 2], a[q * 4 + 3]);
-                        }
-                        const int r = i * 32 + (el & 31), chunk = cb * 4 + q;
-                        *reinterpret_cast<uint2 *>(ep + r * 128 + ((chunk ^ (r & 7)) << 4) +
-                                                   (el >> 5) * 8) = make_uint2(w0, w1);
-                    }
+                    const int r = jb * 16 + (el & 15), col = ib * 16 + (el >> 4) * 4;
+                    const int chunk = col >> 3;
+                    *reinterpret_cast<uint2 *>(ep + r * 128 + ((chunk ^ (r & 7)) << 4) + (col & 4) * 2) =
+                        make_uint2(w0, w1);
                 }
             }
             // A wave reads back only its own block, and LDS operations of
