@@ -1022,6 +1022,8 @@ constexpr uint32_t kGemmGroupM = 8;
 constexpr int kGemmThreads = 256;
 constexpr int kGemmBarrierAt = 48;        // product of step 1 that the barrier precedes
 constexpr int kGemmLoadEvery = 3;         // step 0 issues one load per this many products
+constexpr int kGemmStaggerRow = 4;        // K-walk offset (slices) per row block of a group
+constexpr int kGemmStaggerCol = 1;        // and per column block
 // The barrier must follow the last read of the current stage (the x block
 // read at product 40 of step 1) and precede the first read of the next one
 // (product 48); the loads stay in step 0.
@@ -1088,11 +1090,24 @@ void gemm_gate_up_kernel(GemmParams p)
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     uint32_t ox[8], ow[8];
     const uint16_t *bx = p.x, *bw = p.w;
+    // The tile walks K starting at slice ks0 and wrapping around.  The 32
+    // tiles an XCD works on at once (8 row blocks x 4 column blocks, see
+    // gemm_tile) start kGemmStaggerRow slices apart per row block and
+    // kGemmStaggerCol per column block, so they do not all request the same
+    // 128-byte column window of x and W at the same moment; tiles that share
+    // an x block stay within 3 slices of each other and so still meet its
+    // lines in L2.  (Every tile sums its K slices in its own fixed order,
+    // the same for the plain and the fused product.)
+    const int KT = p.K / kGemmBK;
+    int ks0 = 0;
     auto point = [&](int64_t m0, int32_t n0) {
         int ln = lane;
         asm volatile("" : "+v"(ln));
         bx = p.x + m0 * p.x_stride;
         bw = p.w + ((wv < 2 ? 0 : (int64_t)p.H) + n0) * p.w_stride;
+        ks0 = KT > 0 ? (int)(((m0 / kGemmBM) % kGemmGroupM) * kGemmStaggerRow +
+                             (n0 / kGemmBN) % 4 * kGemmStaggerCol) % KT
+                     : 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int row = 64 * wv + 8 * j + (ln >> 3);
@@ -1120,7 +1135,8 @@ void gemm_gate_up_kernel(GemmParams p)
     const uint32_t lds0 = (uint32_t)(uintptr_t)gsm + kGemmLutBytes + wv * 8 * 1024;
     auto dma1 = [&](int kt, int st, int idx) {
         const int j = idx & 7;
-        const uint16_t *base = (idx < 8 ? bx : bw) + (int64_t)kt * kGemmBK;
+        const int kk = kt + ks0 < KT ? kt + ks0 : kt + ks0 - KT;
+        const uint16_t *base = (idx < 8 ? bx : bw) + (int64_t)kk * kGemmBK;
         const uint32_t off = idx < 8 ? ox[j] : ow[j];
         const uint32_t dst = lds0 + st * kGemmStageBytes + (idx < 8 ? 0 : kGemmOpBytes) + j * 1024;
 #pragma clang diagnostic push
@@ -1163,7 +1179,6 @@ void gemm_gate_up_kernel(GemmParams p)
         acc[jb][ib] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[set][ib], xf[jb & 3], acc[jb][ib], 0, 0, 0);
     };
 
-    const int KT = p.K / kGemmBK;
     uint32_t tile = blockIdx.x;
     int64_t m0;
     int32_t n0;
