@@ -31,8 +31,9 @@ box) and its fraction of that ceiling (`vs_ceiling`).
 workload (16384 tokens, 8192 GEGLU rows): `value` on one thread, and
 `all_cores` with the sample split over every core the process may use;
 `cpu` names the host CPU model.  `roofline.traffic` comes from the committed rocprofv3
-counter summary for the dominant kernel, and is null if the kernel source's
-code (comments aside) has changed since the counters were taken.
+counter summary for the dominant kernel, and is null if the code of the
+step's kernels (comments and the projection kernel aside) has changed since
+the counters were taken.
 
     python bench.py --pmc-summary DIR --pmc-out FILE
 turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE outputs (DIR/fetch, DIR/write)
@@ -90,11 +91,20 @@ COPY_BYTES = 1 << 30
 
 
 def source_digest():
-    """Hash of the kernel source's code: comments and whitespace are dropped,
-    so counters stay current across comment-only edits and go stale with any
-    change to the code itself."""
+    """Hash of the code of the kernels the step runs: comments and whitespace
+    are dropped, and so is the projection kernel (its constants, kernel and
+    launcher), which the step never launches; the counters of the step's
+    kernels stay current across those edits and go stale with any other
+    change to the code of kernels.hip (helpers shared with the projection
+    included)."""
     with open(KERNELS_SRC) as f:
         text = f.read()
+    a = text.index("typedef __bf16 bf16x8")
+    b = text.index("#undef RGG_FENCE")
+    text = text[:a] + text[b:]
+    c = text.index("hipError_t launch_gemm_gate_up(")
+    d = text.index("\n}\n", c)
+    text = text[:c] + text[d + 3:]
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())
