@@ -18,6 +18,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "launch.h"
 
@@ -1283,38 +1284,49 @@ void gemm_gate_up_kernel(GemmParams p)
                         general |= (bf16_of(acc[jb][ib][v]) & 0x7FFFu) - 0x0100u >= kLutHi - 0x0100u;
             anyg = __builtin_amdgcn_ballot_w64(general) != 0;
         }
-#pragma unroll
-        for (int half = 0; half < (Geglu ? 1 : 2); ++half) {
+        // The 32 blocks of a wave go through one branch-free pass, the
+        // table path or the general one (chosen once for the wave above), so
+        // the compiler can keep several blocks' table reads in flight.
+        // Per row of blocks, all 16 table reads go out before the row's
+        // results are written to the staging area (LDS operations stay in
+        // order, so a write between them would hold the next reads back).
+        auto stage = [&](int half, auto general) {
 #pragma unroll
             for (int jb = 0; jb < 8; ++jb) {
+                uint32_t w[4][2];
 #pragma unroll
                 for (int ib = 0; ib < 4; ++ib) {
-                    uint32_t w0, w1;
                     if (Geglu) {
                         float G[4];
-                        if (!anyg) {
 #pragma unroll
-                            for (int v = 0; v < 4; ++v)
-                                G[v] = __uint_as_float(gelu_common(bf16_of(acc[jb][ib][v]), lut));
-                        } else {
-#pragma unroll
-                            for (int v = 0; v < 4; ++v)
-                                G[v] = __uint_as_float(gelu_general(bf16_of(acc[jb][ib][v]), lut) << 16);
-                        }
+                        for (int v = 0; v < 4; ++v)
+                            G[v] = decltype(general)::value
+                                       ? __uint_as_float(gelu_general(bf16_of(acc[jb][ib][v]), lut) << 16)
+                                       : __uint_as_float(gelu_common(bf16_of(acc[jb][ib][v]), lut));
                         const f32x4 &u = acc[jb][ib + 4];
-                        w0 = rne_pack(bf_lo(bf16_of(u[0])) * G[0], bf_lo(bf16_of(u[1])) * G[1]);
-                        w1 = rne_pack(bf_lo(bf16_of(u[2])) * G[2], bf_lo(bf16_of(u[3])) * G[3]);
+                        w[ib][0] = rne_pack(bf_lo(bf16_of(u[0])) * G[0], bf_lo(bf16_of(u[1])) * G[1]);
+                        w[ib][1] = rne_pack(bf_lo(bf16_of(u[2])) * G[2], bf_lo(bf16_of(u[3])) * G[3]);
                     } else {
                         const f32x4 &a = acc[jb][ib + 4 * half];
-                        w0 = rne_pack(a[0], a[1]);
-                        w1 = rne_pack(a[2], a[3]);
+                        w[ib][0] = rne_pack(a[0], a[1]);
+                        w[ib][1] = rne_pack(a[2], a[3]);
                     }
+                }
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib) {
                     const int r = jb * 16 + (el & 15), col = ib * 16 + (el >> 4) * 4;
                     const int chunk = col >> 3;
                     *reinterpret_cast<uint2 *>(ep + r * 128 + ((chunk ^ (r & 7)) << 4) + (col & 4) * 2) =
-                        make_uint2(w0, w1);
+                        make_uint2(w[ib][0], w[ib][1]);
                 }
             }
+        };
+#pragma unroll
+        for (int half = 0; half < (Geglu ? 1 : 2); ++half) {
+            if (anyg)
+                stage(half, std::true_type{});
+            else
+                stage(half, std::false_type{});
             // A wave reads back only its own block, and LDS operations of
             // one wave complete in order: no barrier (which would also wait
             // for the next tile's loads).
