@@ -18,7 +18,6 @@
 
 #include <algorithm>
 #include <mutex>
-#include <type_traits>
 
 #include "launch.h"
 
@@ -1010,6 +1009,10 @@ __global__ __launch_bounds__(kGegluBlock) void gelu_and_mul_kernel(GegluParams p
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <bool B>
+struct GeluPath {  // compile-time choice of the epilogue's GELU path
+    static constexpr bool value = B;
+};
 
 constexpr int kGemmBM = 256;              // rows of x per workgroup
 constexpr int kGemmBN = 128;              // gate (and up) columns per workgroup
@@ -1324,9 +1327,9 @@ void gemm_gate_up_kernel(GemmParams p)
 #pragma unroll
         for (int half = 0; half < (Geglu ? 1 : 2); ++half) {
             if (anyg)
-                stage(half, std::true_type{});
+                stage(half, GeluPath<true>{});
             else
-                stage(half, std::false_type{});
+                stage(half, GeluPath<false>{});
             // A wave reads back only its own block, and LDS operations of
             // one wave complete in order: no barrier (which would also wait
             // for the next tile's loads).
