@@ -197,14 +197,13 @@ int rope_cossin_from_grid(int64_t B, int64_t T, int64_t Hg, int64_t Wg, int32_t 
     p.cos = cos_out;
     p.sin = sin_out;
     p.theta = theta;
-    p.groups_total = (uint32_t)(B * S * (R / 16));
+    p.rows = (uint32_t)(B * S);
     p.R = (int32_t)R;
     p.h0 = d0 / 2;
     p.h01 = (d0 + d1) / 2;
     p.d[0] = d0;
     p.d[1] = d1;
     p.d[2] = d2;
-    p.div_groups = make_fastdiv((uint32_t)(R / 16));
     p.div_s = make_fastdiv((uint32_t)S);
     p.div_hw = make_fastdiv((uint32_t)(Hg * Wg));
     p.div_w = make_fastdiv((uint32_t)Wg);

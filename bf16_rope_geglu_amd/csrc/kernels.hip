@@ -134,11 +134,13 @@ __device__ __forceinline__ void cossin_vec8(v4u a0, v4u a1, uint32_t *c, uint32_
     cossin_pair(__uint_as_float(a1.z), __uint_as_float(a1.w), c[3], sn[3]);
 }
 
-// Paired form (R a multiple of 16): a lane owns columns 8g .. 8g+7 of both
-// halves of a row.  Rotate-half angle tables usually repeat the first half
-// in the second (cat(f, f)); when the eight angles of the second half are
-// bitwise the first half's, their cos/sin are reused instead of recomputed.
-template <bool Paired>
+// Paired form (R a multiple of 16): a lane owns W consecutive columns of
+// both halves of a row (W = 8, or 4 for Narrow).  Rotate-half angle tables
+// usually repeat the first half in the second (cat(f, f)); when the W angles
+// of the second half are bitwise the first half's, their cos/sin are reused
+// instead of recomputed.  Narrow lanes do half the work each, which pays
+// while the table is small enough that all lanes run at once (kTableNarrowLanes).
+template <bool Paired, bool Narrow>
 __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
 {
     const uint32_t nvec_row = p.div_vecs.d;
@@ -157,7 +159,25 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
         uint32_t s = row - b * S;
         const float *f = p.freqs + (int64_t)s * p.stride_s + (int64_t)b * p.stride_b;
         int64_t o = (int64_t)row * p.R;
-        if constexpr (Paired) {
+        if constexpr (Paired && Narrow) {
+            const int col = cg * 4;
+            uint32_t c[2], sn[2];
+            const v4u a0 = *reinterpret_cast<const v4u *>(f + col);
+            const v4u b0 = *reinterpret_cast<const v4u *>(f + half + col);
+            cossin_pair(__uint_as_float(a0.x), __uint_as_float(a0.y), c[0], sn[0]);
+            cossin_pair(__uint_as_float(a0.z), __uint_as_float(a0.w), c[1], sn[1]);
+            uint2 cv = make_uint2(c[0], c[1]), sv = make_uint2(sn[0], sn[1]);
+            *reinterpret_cast<uint2 *>(p.cos + o + col) = cv;
+            *reinterpret_cast<uint2 *>(p.sin + o + col) = sv;
+            if (!(a0.x == b0.x && a0.y == b0.y && a0.z == b0.z && a0.w == b0.w)) {
+                cossin_pair(__uint_as_float(b0.x), __uint_as_float(b0.y), c[0], sn[0]);
+                cossin_pair(__uint_as_float(b0.z), __uint_as_float(b0.w), c[1], sn[1]);
+                cv = make_uint2(c[0], c[1]);
+                sv = make_uint2(sn[0], sn[1]);
+            }
+            *reinterpret_cast<uint2 *>(p.cos + o + half + col) = cv;
+            *reinterpret_cast<uint2 *>(p.sin + o + half + col) = sv;
+        } else if constexpr (Paired) {
             const int col = cg * 8;
             uint32_t c[4], sn[4];
             v4u a0 = *reinterpret_cast<const v4u *>(f + col);
@@ -198,16 +218,23 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
 // Token s of a (T, Hg, Wg) grid sits at (t, h, w), s = (t*Hg + h)*Wg + w,
 // with t shifted by the batch row's offset.  Half-column c of axis k (local
 // index i) turns by pos_k * theta^(-2i/d_k), formed in double and rounded once
-// to fp32, and the row is cat(f, f), so a lane computes 8 half-columns and
-// stores each cos/sin vector in both halves.  Each workgroup first puts the
+// to fp32, and the row is cat(f, f), so a lane computes W half-columns (8, or
+// 4 for small tables as in the precompute) and stores each cos/sin vector in
+// both halves.  Each workgroup first puts the
 // frequencies theta^(-2i/d_k) of the R/2 half-columns in LDS: copied from the
 // kernel arguments (computed on the host) for up to 2*kGridOmegaArgs rotary
 // columns, evaluated on the device for wider rows.  The cos/sin of the fp32
 // angle then go through the same correctly rounded path as the precompute
 // above.
 // ---------------------------------------------------------------------------
+template <int W> struct TableVec { using type = v4u; };    // 8 bf16
+template <> struct TableVec<4> { using type = uint2; };   // 4 bf16
+
+template <int W>
 __global__ __launch_bounds__(kThreads) void rope_cossin_grid_kernel(CosSinGridParams p)
 {
+    static_assert(W == 4 || W == 8, "a lane stores one 8- or 16-byte vector per table half");
+    using vec = typename TableVec<W>::type;
     extern __shared__ double lomega[];  // [R/2]
     const int half = p.R / 2;
     for (int c = threadIdx.x; c < half; c += kThreads) {
@@ -224,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_grid_kernel(CosSinGridPa
     for (uint32_t g = blockIdx.x * kThreads + threadIdx.x; g < p.groups_total;
          g += gridDim.x * kThreads) {
         const uint32_t row = fdiv(g, p.div_groups);
-        const int c0 = (int)(g - row * groups) * 8;
+        const int c0 = (int)(g - row * groups) * W;
         const uint32_t b = fdiv(row, p.div_s);
         const uint32_t s = row - b * S;
         const uint32_t t = fdiv(s, p.div_hw);
@@ -233,23 +260,23 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_grid_kernel(CosSinGridPa
         const uint32_t w = hw - h * Wg;
         const double pos[3] = {(double)((int64_t)t + (p.t_offset ? p.t_offset[b] : 0)),
                                (double)h, (double)w};
-        float a[8];
+        float a[W];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < W; ++e) {
             const int c = c0 + e;
             const int k = c < p.h0 ? 0 : (c < p.h01 ? 1 : 2);
             a[e] = __double2float_rn(pos[k] * lomega[c]);
         }
-        uint32_t cw[4], sw[4];
+        vec cv, sv;
+        uint32_t *cw = reinterpret_cast<uint32_t *>(&cv), *sw = reinterpret_cast<uint32_t *>(&sv);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < W / 2; ++q)
             cossin_pair(a[2 * q], a[2 * q + 1], cw[q], sw[q]);
-        const v4u cv = v4u{cw[0], cw[1], cw[2], cw[3]}, sv = v4u{sw[0], sw[1], sw[2], sw[3]};
         const int64_t o = (int64_t)row * p.R + c0;
-        *reinterpret_cast<v4u *>(p.cos + o) = cv;
-        *reinterpret_cast<v4u *>(p.cos + o + half) = cv;
-        *reinterpret_cast<v4u *>(p.sin + o) = sv;
-        *reinterpret_cast<v4u *>(p.sin + o + half) = sv;
+        *reinterpret_cast<vec *>(p.cos + o) = cv;
+        *reinterpret_cast<vec *>(p.cos + o + half) = cv;
+        *reinterpret_cast<vec *>(p.sin + o) = sv;
+        *reinterpret_cast<vec *>(p.sin + o + half) = sv;
     }
 }
 
@@ -1369,26 +1396,37 @@ hipError_t launch_rope_cossin(const CosSinParams &params, hipStream_t stream)
     CosSinParams p = params;
     const uint32_t rows = p.vec_total / (uint32_t)(p.R / 8);
     const bool paired = p.R % 16 == 0;
-    const uint32_t per_row = paired ? (uint32_t)(p.R / 16) : (uint32_t)(p.R / 8);
+    const bool narrow = paired && (uint64_t)rows * (uint32_t)(p.R / 8) <= kTableNarrowLanes;
+    const uint32_t per_row = paired && !narrow ? (uint32_t)(p.R / 16) : (uint32_t)(p.R / 8);
     p.vec_total = rows * per_row;
     p.div_vecs = make_fastdiv(per_row);
     uint32_t blocks = (p.vec_total + kThreads - 1) / kThreads;
     if (blocks > 4096)
         blocks = 4096;
-    if (paired)
-        hipLaunchKernelGGL(rope_cossin_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, p);
+    if (narrow)
+        hipLaunchKernelGGL((rope_cossin_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    else if (paired)
+        hipLaunchKernelGGL((rope_cossin_kernel<true, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL(rope_cossin_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((rope_cossin_kernel<false, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_rope_cossin_grid(const CosSinGridParams &p, hipStream_t stream)
+hipError_t launch_rope_cossin_grid(const CosSinGridParams &params, hipStream_t stream)
 {
+    CosSinGridParams p = params;
+    const bool narrow = (uint64_t)p.rows * (uint32_t)(p.R / 8) <= kTableNarrowLanes;
+    const uint32_t per_row = (uint32_t)(p.R / (narrow ? 8 : 16));
+    p.groups_total = p.rows * per_row;
+    p.div_groups = make_fastdiv(per_row);
     uint32_t blocks = (p.groups_total + kThreads - 1) / kThreads;
     if (blocks > 2048)
         blocks = 2048;
     const size_t lds = (size_t)(p.R / 2) * sizeof(double);
-    hipLaunchKernelGGL(rope_cossin_grid_kernel, dim3(blocks), dim3(kThreads), lds, stream, p);
+    if (narrow)
+        hipLaunchKernelGGL(rope_cossin_grid_kernel<4>, dim3(blocks), dim3(kThreads), lds, stream, p);
+    else
+        hipLaunchKernelGGL(rope_cossin_grid_kernel<8>, dim3(blocks), dim3(kThreads), lds, stream, p);
     return hipGetLastError();
 }
 

@@ -76,6 +76,12 @@ struct CosSinParams {
     FastDiv div_s;         // row -> (b, s)
 };
 
+// Below this many lanes of 4 columns, the cos/sin table kernels give each
+// lane 4 columns of each half instead of 8: all lanes then run at once, and
+// halving the work per lane shortens the launch.  Above it the wider lanes
+// are faster (fewer rounds of address arithmetic per byte).
+constexpr uint64_t kTableNarrowLanes = 1u << 18;
+
 constexpr int kGridOmegaArgs = 256;  // half-column frequencies carried in the kernel arguments
 
 struct CosSinGridParams {
@@ -83,11 +89,12 @@ struct CosSinGridParams {
     uint16_t *cos;
     uint16_t *sin;
     double theta;
-    uint32_t groups_total;     // B * S * (R / 16): lanes of 8 half-columns
+    uint32_t rows;             // B * S
+    uint32_t groups_total;     // rows * (R / W): lanes of W half-columns (set by the launcher)
     int32_t R;
     int32_t h0, h01;           // d0/2 and (d0 + d1)/2: first half-column of axes 1 and 2
     int32_t d[3];
-    FastDiv div_groups;        // divisor R / 16: lane -> (row, group)
+    FastDiv div_groups;        // divisor R / W: lane -> (row, group) (set by the launcher)
     FastDiv div_s;             // row -> (b, s)
     FastDiv div_hw;            // s -> (t, h*Wg + w)
     FastDiv div_w;             // h*Wg + w -> (h, w)

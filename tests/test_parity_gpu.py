@@ -112,11 +112,12 @@ def test_cossin_adversarial(orc):
     assert_ulp_bar(host(s), os_, "sin strided")
 
 
-def test_cossin_mixed_paired_rows(orc):
+@pytest.mark.parametrize("S,B,R", [(97, 3, 32), (4099, 3, 256)], ids=["narrow", "wide"])
+def test_cossin_mixed_paired_rows(orc, S, B, R):
     """Rows whose two halves repeat (cat(f, f)) next to rows whose halves
-    differ, in the same waves: both branches of the paired table kernel."""
-    say("cos/sin mixed paired / unpaired rows")
-    S, B, R = 97, 3, 32
+    differ, in the same waves: both branches of the paired table kernel, with
+    4 columns per lane (small table) and with 8 (over 2^18 lanes of 4)."""
+    say(f"cos/sin mixed paired / unpaired rows S={S} B={B} R={R}")
     fr = W.freqs_unpaired(S, B, R, 4040)
     rep = (np.arange(S) % 3) == 0
     fr[rep, :, :, R // 2:] = fr[rep, :, :, :R // 2]
@@ -156,6 +157,7 @@ GRID_TABLES = [  # B, grid, dims, theta, t_offset
     (2, (5, 1, 9), (0, 16, 16), 256.0, [7, -3]),     # an axis with no columns
     (1, (1, 2, 3), (2, 6, 8), 1e6, None),            # one 8-column group per row
     (2, (2, 3, 5), (256, 256, 128), 1e4, [3, 0]),    # R = 640: frequencies built on the device
+    (2, (3, 67, 41), (32, 48, 48), 1e4, [0, 2]),     # ragged, just over 2^18 lanes of 4 columns
 ]
 
 
