@@ -92,8 +92,9 @@ __device__ __forceinline__ uint32_t bf16_from_double(double v)
 // ---------------------------------------------------------------------------
 // Cos/sin tables                             [ERNIE-fuse §1]
 //
-// One lane per 8 consecutive rotary columns of one table row: two 16-byte
-// angle loads, eight fp32 sincosf, two 16-byte stores.  sincosf is accurate
+// A lane owns a run of consecutive rotary columns of one table row (8, or 4
+// of each half in small paired tables): vector angle loads, one fp32 sincosf
+// per angle, vector stores of cos and sin.  sincosf is accurate
 // to a couple of fp32 ulps, so rounding its result to bf16 gives the
 // correctly rounded bf16 of the true value unless the fp32 result lies within
 // a few ulps of a bf16 rounding midpoint (its low 16 bits near 0x8000).
