@@ -129,6 +129,22 @@ def test_cossin_mixed_paired_rows(orc, S, B, R):
     assert_ulp_bar(gs, os_, "sin mixed rows")
 
 
+@pytest.mark.parametrize("S,B", [(8192, 2), (16385, 1)], ids=["at_threshold", "one_row_over"])
+def test_cossin_lane_threshold(orc, S, B):
+    """Tables of exactly 2^18 lanes of 4 columns (R = 128: 16384 rows) take
+    the 4-column lanes, one row more the 8-column lanes; both match the
+    oracle, with halves that repeat and halves that differ."""
+    say(f"cos/sin at the lane threshold S={S} B={B}")
+    R = 128
+    fr = W.freqs_unpaired(S, B, R, 5150)
+    rep = (np.arange(S) % 2) == 0
+    fr[rep, :, :, R // 2:] = fr[rep, :, :, :R // 2]
+    gc, gs = gpu_cossin(fr)
+    oc, os_ = orc.rope_cossin(fr)
+    assert_ulp_bar(gc, oc, "cos at threshold")
+    assert_ulp_bar(gs, os_, "sin at threshold")
+
+
 def test_cossin_empty_and_guards(orc):
     say("cos/sin empty shapes and guard bands")
     f = torch.zeros((0, 2, 1, 16), device="cuda")
@@ -158,6 +174,8 @@ GRID_TABLES = [  # B, grid, dims, theta, t_offset
     (1, (1, 2, 3), (2, 6, 8), 1e6, None),            # one 8-column group per row
     (2, (2, 3, 5), (256, 256, 128), 1e4, [3, 0]),    # R = 640: frequencies built on the device
     (2, (3, 67, 41), (32, 48, 48), 1e4, [0, 2]),     # ragged, just over 2^18 lanes of 4 columns
+    (1, (4, 64, 64), (32, 48, 48), 1e4, None),       # exactly 2^18 lanes of 4 columns
+    (5, (1, 29, 113), (32, 48, 48), 1e4, [0, 1, 2, 3, 4]),  # 16385 rows: one row over
 ]
 
 
