@@ -139,8 +139,9 @@ __device__ __forceinline__ void cossin_vec8(v4u a0, v4u a1, uint32_t *c, uint32_
 // both halves of a row (W = 8, or 4 for Narrow).  Rotate-half angle tables
 // usually repeat the first half in the second (cat(f, f)); when the W angles
 // of the second half are bitwise the first half's, their cos/sin are reused
-// instead of recomputed.  Narrow lanes do half the work each, which pays
-// while the table is small enough that all lanes run at once (kTableNarrowLanes).
+// instead of recomputed.  Narrow lanes do half the work each: for small
+// tables (up to kTableNarrowLanes of them) twice as many lanes fill more of
+// the chip and each lane's chain of sincos is half as long.
 template <bool Paired, bool Narrow>
 __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
 {
