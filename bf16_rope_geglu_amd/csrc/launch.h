@@ -76,10 +76,10 @@ struct CosSinParams {
     FastDiv div_s;         // row -> (b, s)
 };
 
-// Below this many lanes of 4 columns, the cos/sin table kernels give each
-// lane 4 columns of each half instead of 8: all lanes then run at once, and
-// halving the work per lane shortens the launch.  Above it the wider lanes
-// are faster (fewer rounds of address arithmetic per byte).
+// Up to this many lanes of 4 columns, the cos/sin table kernels give each
+// lane 4 columns of each half instead of 8: twice as many lanes fill more of
+// the chip, and each lane's chain of sincos is half as long.  Above it the
+// 8-column lanes are faster (measured at 2^19 lanes of 4).
 constexpr uint64_t kTableNarrowLanes = 1u << 18;
 
 constexpr int kGridOmegaArgs = 256;  // half-column frequencies carried in the kernel arguments
