@@ -81,6 +81,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused RoPE + GEGLU effective HBM GB/s and % of MI355X peak (bf16)"
 PEAK_HBM_GBPS = 8000.0
 KERNELS_SRC = os.path.join(ROOT, "bf16_rope_geglu_amd", "csrc", "kernels.hip")
+LAUNCH_H = os.path.join(ROOT, "bf16_rope_geglu_amd", "csrc", "launch.h")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gelu_and_mul_dit_layer_traffic.md")
 KERNEL_SYMBOL = {
     "precompute": "rope_cossin_kernel",
@@ -91,12 +92,13 @@ COPY_BYTES = 1 << 30
 
 
 def source_digest():
-    """Hash of the code of the kernels the step runs: comments and whitespace
-    are dropped, and so is the projection kernel (its constants, kernel and
-    launcher), which the step never launches; the counters of the step's
-    kernels stay current across those edits and go stale with any other
-    change to the code of kernels.hip (helpers shared with the projection
-    included)."""
+    """Hash of the code of the kernels the step runs: kernels.hip and
+    launch.h (parameter blocks, launch thresholds), with comments and
+    whitespace dropped, and without the projection kernel (its constants,
+    kernel and launcher), which the step never launches.  The counters of
+    the step's kernels stay current across those edits and go stale with any
+    other change to the code of either file (helpers shared with the
+    projection included)."""
     with open(KERNELS_SRC) as f:
         text = f.read()
     a = text.index("typedef __bf16 bf16x8")
@@ -105,6 +107,8 @@ def source_digest():
     c = text.index("hipError_t launch_gemm_gate_up(")
     d = text.index("\n}\n", c)
     text = text[:c] + text[d + 3:]
+    with open(LAUNCH_H) as f:
+        text += "\n" + f.read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())

@@ -451,3 +451,27 @@ def test_counter_summary_medians(tmp_path):
     assert header == ["gemm_gate_up_kernel<false>", "hipBLASLt GEMM (torch.matmul)"]
     assert table["GRBM_GUI_ACTIVE"] == ["20", "7"]      # dispatch 1 sums to 15; median of 15, 30, 20
     assert table["MfmaUtil"] == ["70", ""]
+
+
+def test_source_digest_tracks_step_code_not_comments(tmp_path, monkeypatch):
+    """bench.py keys the committed counter traffic to a digest of the step
+    kernels' code: comments and the projection kernel do not move it, any
+    other code change in kernels.hip or launch.h does."""
+    import bench
+    src = open(bench.KERNELS_SRC).read()
+    lh = open(bench.LAUNCH_H).read()
+    k, h = tmp_path / "kernels.hip", tmp_path / "launch.h"
+    k.write_text(src)
+    h.write_text(lh)
+    monkeypatch.setattr(bench, "KERNELS_SRC", str(k))
+    monkeypatch.setattr(bench, "LAUNCH_H", str(h))
+    d0 = bench.source_digest()
+    h.write_text(lh + "\n// a comment\n/* another */\n")
+    assert bench.source_digest() == d0
+    h.write_text(lh.replace("kTableNarrowLanes = 1u << 18", "kTableNarrowLanes = 1u << 17"))
+    assert bench.source_digest() != d0
+    h.write_text(lh)
+    k.write_text(src.replace("kGemmStaggerRow = 4", "kGemmStaggerRow = 3"))
+    assert bench.source_digest() == d0
+    k.write_text(src.replace("constexpr uint32_t kTieGuard = 4;", "constexpr uint32_t kTieGuard = 5;"))
+    assert bench.source_digest() != d0
