@@ -1067,8 +1067,6 @@ static_assert(kGemmLutBytes % 1024 == 0, "stages start on a 1 KiB boundary");
 static_assert(4 * 128 * 64 * 2 <= kGemmStageBytes, "epilogue blocks fit stage 1");
 static_assert(kLutEntries % 8 == 0 && kLutEntries / 8 <= 2 * kGemmThreads, "table: two vectors per lane");
 
-__device__ __forceinline__ uint32_t bf16_of(float v) { return rne_pack(v, 0.0f) & 0xFFFFu; }
-
 #define RGG_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Tile t of T (in launch order) -> (row block, column block): the XCD run
@@ -1305,6 +1303,10 @@ void gemm_gate_up_kernel(GemmParams p)
         const int32_t cbase = cn0 + wn * 64;
         const bool live = cbase < p.H;
         bool anyg = false;
+        // The gates rounded to bf16 once, two to a word, for both the path
+        // test and the table reads: gp[jb][ib][0] holds the lane's columns 0
+        // and 1 of block (jb, ib), [1] columns 2 and 3.
+        uint32_t gp[8][4][2];
         if (Geglu) {
             bool general = false;
 #pragma unroll
@@ -1312,8 +1314,12 @@ void gemm_gate_up_kernel(GemmParams p)
 #pragma unroll
                 for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        general |= (bf16_of(acc[jb][ib][v]) & 0x7FFFu) - 0x0100u >= kLutHi - 0x0100u;
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t w = rne_pack(acc[jb][ib][2 * h], acc[jb][ib][2 * h + 1]);
+                        gp[jb][ib][h] = w;
+                        general |= (w & 0x7FFFu) - 0x0100u >= kLutHi - 0x0100u;
+                        general |= ((w >> 16) & 0x7FFFu) - 0x0100u >= kLutHi - 0x0100u;
+                    }
             anyg = __builtin_amdgcn_ballot_w64(general) != 0;
         }
         // The 32 blocks of a wave go through one branch-free pass, the
@@ -1331,13 +1337,16 @@ void gemm_gate_up_kernel(GemmParams p)
                     if (Geglu) {
                         float G[4];
 #pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            G[v] = decltype(general)::value
-                                       ? __uint_as_float(gelu_general(bf16_of(acc[jb][ib][v]), lut) << 16)
-                                       : __uint_as_float(gelu_common(bf16_of(acc[jb][ib][v]), lut));
+                        for (int v = 0; v < 4; ++v) {
+                            const uint32_t g = (gp[jb][ib][v >> 1] >> (16 * (v & 1))) & 0xFFFFu;
+                            G[v] = decltype(general)::value ? __uint_as_float(gelu_general(g, lut) << 16)
+                                                            : __uint_as_float(gelu_common(g, lut));
+                        }
+                        // up rounded to bf16 two at a time, then widened back
                         const f32x4 &u = acc[jb][ib + 4];
-                        w[ib][0] = rne_pack(bf_lo(bf16_of(u[0])) * G[0], bf_lo(bf16_of(u[1])) * G[1]);
-                        w[ib][1] = rne_pack(bf_lo(bf16_of(u[2])) * G[2], bf_lo(bf16_of(u[3])) * G[3]);
+                        const uint32_t u01 = rne_pack(u[0], u[1]), u23 = rne_pack(u[2], u[3]);
+                        w[ib][0] = rne_pack(bf_lo(u01) * G[0], bf_hi(u01) * G[1]);
+                        w[ib][1] = rne_pack(bf_lo(u23) * G[2], bf_hi(u23) * G[3]);
                     } else {
                         const f32x4 &a = acc[jb][ib + 4 * half];
                         w[ib][0] = rne_pack(a[0], a[1]);
