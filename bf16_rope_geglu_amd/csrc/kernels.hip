@@ -222,12 +222,11 @@ __global__ __launch_bounds__(kThreads) void rope_cossin_kernel(CosSinParams p)
 // index i) turns by pos_k * theta^(-2i/d_k), formed in double and rounded once
 // to fp32, and the row is cat(f, f), so a lane computes W half-columns (8, or
 // 4 for small tables as in the precompute) and stores each cos/sin vector in
-// both halves.  Each workgroup first puts the
-// frequencies theta^(-2i/d_k) of the R/2 half-columns in LDS: copied from the
-// kernel arguments (computed on the host) for up to 2*kGridOmegaArgs rotary
-// columns, evaluated on the device for wider rows.  The cos/sin of the fp32
-// angle then go through the same correctly rounded path as the precompute
-// above.
+// both halves.  Each workgroup first puts the frequencies theta^(-2i/d_k) of
+// the R/2 half-columns in LDS: copied from the kernel arguments (computed on
+// the host) for up to 2*kGridOmegaArgs rotary columns, evaluated on the
+// device for wider rows.  The cos/sin of the fp32 angle then go through the
+// same correctly rounded path as the precompute above.
 // ---------------------------------------------------------------------------
 template <int W> struct TableVec { using type = v4u; };    // 8 bf16
 template <> struct TableVec<4> { using type = uint2; };   // 4 bf16
